@@ -1,0 +1,19 @@
+"""MI355X-native staged decode attention for beam-search generative recommendation.
+
+The compute path is the C-ABI library ``libxattn.so`` (hand-written HIP
+kernels for gfx950, declared in ``include/xattn.h``); this package is its
+thin Python binding.  The binding loads the library on first use and raises
+if it is missing: there is no fallback implementation.
+"""
+from . import workloads  # noqa: F401  (seeded inputs; no attention arithmetic)
+
+__all__ = ["decode", "decode_debug", "resolve_ancestors", "workspace_size", "library_path",
+           "XattnError", "workloads"]
+
+
+def __getattr__(name):
+    if name in ("decode", "decode_debug", "resolve_ancestors", "workspace_size",
+                "library_path", "XattnError", "load"):
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)
