@@ -1,0 +1,207 @@
+"""ctypes binding of libxattn.so (include/xattn.h).
+
+Argument marshalling only: shapes are read off the tensors, pointers and the
+current HIP stream are passed through, and every step of the computation runs
+in the library's kernels.  PyTorch supplies device memory and streams.  If
+the library has not been built this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
+
+XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EHIP = 0, 1, 2, 3
+XATTN_F32, XATTN_BF16 = 0, 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class XattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("xattn status %d: %s" % (status, msg))
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("num_requests", ctypes.c_int32), ("beam_width", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("max_prompt_len", ctypes.c_int32),
+                ("max_steps", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_workspace_size",
+           "xattn_resolve_ancestors", "xattn_status_string", "xattn_last_error")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load():
+    """Load libxattn.so (once) and declare its C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise XattnError(XATTN_EHIP, "libxattn.so is not built (%s); run "
+                             "python -m generative_recommendation_beam_xattn_amd.build" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.POINTER(Shape)
+        i32, sz = ctypes.c_int32, ctypes.c_size_t
+        lib.xattn_decode.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P]
+        lib.xattn_decode.restype = ctypes.c_int
+        lib.xattn_decode_debug.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
+        lib.xattn_decode_debug.restype = ctypes.c_int
+        lib.xattn_workspace_size.argtypes = [S, i32]
+        lib.xattn_workspace_size.restype = sz
+        lib.xattn_resolve_ancestors.argtypes = [S, P, i32, P, P]
+        lib.xattn_resolve_ancestors.restype = ctypes.c_int
+        lib.xattn_status_string.argtypes = [ctypes.c_int]
+        lib.xattn_status_string.restype = ctypes.c_char_p
+        lib.xattn_last_error.argtypes = []
+        lib.xattn_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != XATTN_OK:
+        lib = load()
+        raise XattnError(status, lib.xattn_last_error().decode() or
+                         lib.xattn_status_string(status).decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    if t.dtype == torch.float32:
+        return XATTN_F32
+    if t.dtype == torch.bfloat16:
+        return XATTN_BF16
+    raise ValueError("q, k, v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def make_shape(q, shared_k, unshared_k, scale: float = 0.0) -> Shape:
+    """xattn_shape from q [R][BW][Hq][D], shared_k [R][Hkv][Lmax][D],
+    unshared_k [R][Hkv][S][BW][D]."""
+    R, BW, Hq, D = q.shape
+    Lmax = shared_k.shape[2]
+    S = unshared_k.shape[2]
+    Hkv = shared_k.shape[1]
+    return Shape(R, BW, Hq, Hkv, D, Lmax, S, _dtype_code(q), float(scale or 0.0))
+
+
+def _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx):
+    R, BW, Hq, D = q.shape
+    Hkv = shared_k.shape[1]
+    S = unshared_k.shape[2]
+    if shared_k.dim() != 4 or shared_k.shape[0] != R or shared_k.shape[3] != D:
+        raise ValueError("shared_k must be [R][Hkv][Lmax][D]")
+    if shared_v.shape != shared_k.shape:
+        raise ValueError("shared_v must match shared_k")
+    if tuple(unshared_k.shape) != (R, Hkv, S, BW, D) or unshared_v.shape != unshared_k.shape:
+        raise ValueError("unshared_k/v must be [R][Hkv][S][BW][D]")
+    if tuple(prompt_len.shape) != (R,) or prompt_len.dtype != torch.int32:
+        raise ValueError("prompt_len must be int32 [R]")
+    if tuple(parent_idx.shape) != (R, S, BW) or parent_idx.dtype != torch.int32:
+        raise ValueError("parent_idx must be int32 [R][S][BW]")
+    for t in (shared_k, shared_v, unshared_k, unshared_v):
+        if t.dtype != q.dtype:
+            raise ValueError("q, k and v must share one dtype")
+        if t.device != q.device:
+            raise ValueError("all tensors must be on one device")
+
+
+def workspace_size(shape: Shape, step: int) -> int:
+    n = load().xattn_workspace_size(ctypes.byref(shape), int(step))
+    if n == ctypes.c_size_t(-1).value:
+        raise XattnError(XATTN_EINVAL, "invalid shape or step")
+    return int(n)
+
+
+def _workspace(shape, step, workspace, device):
+    n = load().xattn_workspace_size(ctypes.byref(shape), int(step))
+    if n == ctypes.c_size_t(-1).value:
+        # invalid shape: the entry point itself reports the precise status
+        return None, 0
+    need = int(n)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def decode(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+           out=None, workspace=None, scale: float = 0.0, stream=None):
+    """One decode step of staged attention; returns out [R][BW][Hq][D]."""
+    lib = load()
+    _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
+    shape = make_shape(q, shared_k, unshared_k, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, ws_bytes = _workspace(shape, step, workspace, q.device)
+    _check(lib.xattn_decode(ctypes.byref(shape), _ptr(q), _ptr(shared_k), _ptr(shared_v),
+                            _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v),
+                            _ptr(parent_idx), int(step), _ptr(out), _ptr(ws), ws_bytes,
+                            _stream(stream, q.device)))
+    return out
+
+
+def decode_debug(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+                 scale: float = 0.0, stream=None, lse=True, stages=True):
+    """Staged decode with explicit merge; returns (out, lse, stage_ml, stage_o).
+
+    stage_ml is [2][R][BW][Hq][2] (m, l) and stage_o [2][R][BW][Hq][D], stage 0
+    Shared and stage 1 Unshared; taps not requested come back as None.
+    """
+    lib = load()
+    _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
+    shape = make_shape(q, shared_k, unshared_k, scale)
+    R, BW, Hq, D = q.shape
+    dev = q.device
+    out = torch.empty_like(q)
+    lse_t = torch.empty((R, BW, Hq), dtype=torch.float32, device=dev) if lse else None
+    ml_t = torch.empty((2, R, BW, Hq, 2), dtype=torch.float32, device=dev) if stages else None
+    o_t = torch.empty((2, R, BW, Hq, D), dtype=torch.float32, device=dev) if stages else None
+    ws, ws_bytes = _workspace(shape, step, None, dev)
+    _check(lib.xattn_decode_debug(ctypes.byref(shape), _ptr(q), _ptr(shared_k), _ptr(shared_v),
+                                  _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v),
+                                  _ptr(parent_idx), int(step), _ptr(out), _ptr(lse_t),
+                                  _ptr(ml_t), _ptr(o_t), _ptr(ws), ws_bytes,
+                                  _stream(stream, dev)))
+    return out, lse_t, ml_t, o_t
+
+
+def resolve_ancestors(parent_idx, step: int, stream=None):
+    """anc [R][BW][step+1] int32: ancestor slot of every beam at every level."""
+    lib = load()
+    if parent_idx.dtype != torch.int32 or parent_idx.dim() != 3:
+        raise ValueError("parent_idx must be int32 [R][S][BW]")
+    R, S, BW = parent_idx.shape
+    shape = Shape(R, BW, 1, 1, 64, 0, S, XATTN_BF16, 0.0)
+    anc = torch.empty((R, BW, step + 1), dtype=torch.int32, device=parent_idx.device)
+    _check(lib.xattn_resolve_ancestors(ctypes.byref(shape), _ptr(parent_idx), int(step),
+                                       _ptr(anc), _stream(stream, parent_idx.device)))
+    return anc

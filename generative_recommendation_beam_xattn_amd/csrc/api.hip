@@ -1,0 +1,189 @@
+// C ABI of libxattn.so (declared in include/xattn.h): argument validation,
+// tiling choice and kernel dispatch on the caller's stream.  Nothing here
+// touches device memory; every check below runs before anything is enqueued.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/xattn.h"
+#include "xattn_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+xattn_status fail(xattn_status st, const char *msg) {
+  snprintf(g_last_error, sizeof g_last_error, "%s", msg);
+  return st;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // per tensor, keeps 64-bit offsets far from overflow
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+xattn_status check_shape(const xattn_shape *s, int32_t step) {
+  if (!s) return fail(XATTN_EINVAL, "shape is NULL");
+  if (s->num_requests < 1) return fail(XATTN_EINVAL, "num_requests must be >= 1");
+  if (s->beam_width < 1) return fail(XATTN_EINVAL, "beam_width must be >= 1");
+  if (s->num_kv_heads < 1 || s->num_q_heads < 1)
+    return fail(XATTN_EINVAL, "head counts must be >= 1");
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(XATTN_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+  if (s->max_prompt_len < 0) return fail(XATTN_EINVAL, "max_prompt_len must be >= 0");
+  if (s->max_steps < 1) return fail(XATTN_EINVAL, "max_steps must be >= 1");
+  if (step < 0 || step >= s->max_steps) return fail(XATTN_EINVAL, "step must be in [0, max_steps)");
+  if (!(s->scale >= 0.f) || !isfinite(s->scale))
+    return fail(XATTN_EINVAL, "scale must be finite and >= 0");
+  if (s->dtype != XATTN_F32 && s->dtype != XATTN_BF16) return fail(XATTN_EINVAL, "unknown dtype");
+  if (s->head_dim < 1) return fail(XATTN_EINVAL, "head_dim must be >= 1");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(XATTN_EUNSUPPORTED, "head_dim must be 64 or 128");
+  const int64_t R = s->num_requests, BW = s->beam_width, Hq = s->num_q_heads,
+                Hkv = s->num_kv_heads, D = s->head_dim, Lmax = s->max_prompt_len,
+                S = s->max_steps;
+  const double q_elems = (double)R * BW * Hq * D;
+  const double sh_elems = (double)R * Hkv * Lmax * D;
+  const double un_elems = (double)R * Hkv * S * BW * D;
+  const double par_elems = (double)R * S * BW;
+  if (q_elems > kMaxElems || sh_elems > kMaxElems || un_elems > kMaxElems || par_elems > kMaxElems)
+    return fail(XATTN_EINVAL, "a tensor exceeds 2^40 elements");
+  if ((double)BW * (Hq / Hkv) > 0x7fffffff) return fail(XATTN_EINVAL, "beam_width * group too large");
+  return XATTN_OK;
+}
+
+bool deep_chain(int32_t step) { return step + 1 > xattn::kMaxInKernelLevels; }
+
+size_t workspace_bytes_for(const xattn_shape *s, int32_t step) {
+  if (!deep_chain(step)) return 0;
+  const size_t n = (size_t)s->num_requests * (size_t)(step + 1) * (size_t)s->beam_width;
+  return (n * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
+xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, const void *shared_v,
+                 const int32_t *prompt_len, const void *unshared_k, const void *unshared_v,
+                 const int32_t *parent_idx, int32_t step, void *out, float *lse,
+                 float *stage_ml, float *stage_o, bool taps, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+  xattn_status st = check_shape(s, step);
+  if (st != XATTN_OK) return st;
+  if (!q || !prompt_len || !unshared_k || !unshared_v || !parent_idx || !out)
+    return fail(XATTN_EINVAL, "a required pointer is NULL");
+  if (s->max_prompt_len > 0 && (!shared_k || !shared_v))
+    return fail(XATTN_EINVAL, "shared_k/shared_v are NULL but max_prompt_len > 0");
+  const void *vec[] = {q, shared_k, shared_v, unshared_k, unshared_v, out};
+  for (const void *v : vec)
+    if (!aligned(v, 16)) return fail(XATTN_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(prompt_len, 4) || !aligned(parent_idx, 4))
+    return fail(XATTN_EINVAL, "int32 arrays must be 4-byte aligned");
+  if ((lse && !aligned(lse, 4)) || (stage_ml && !aligned(stage_ml, 4)) ||
+      (stage_o && !aligned(stage_o, 4)))
+    return fail(XATTN_EINVAL, "tap arrays must be 4-byte aligned");
+  const size_t need = workspace_bytes_for(s, step);
+  if (need > 0) {
+    if (!workspace) return fail(XATTN_EINVAL, "this step needs a workspace (xattn_workspace_size)");
+    if (workspace_bytes < need) return fail(XATTN_EINVAL, "workspace is smaller than xattn_workspace_size");
+    if (!aligned(workspace, 256)) return fail(XATTN_EINVAL, "workspace must be 256-byte aligned");
+  }
+
+  xattn::DecodeParams p{};
+  p.q = q;
+  p.shared_k = shared_k;
+  p.shared_v = shared_v;
+  p.prompt_len = prompt_len;
+  p.unshared_k = unshared_k;
+  p.unshared_v = unshared_v;
+  p.parent_idx = parent_idx;
+  p.out = out;
+  p.lse = lse;
+  p.stage_ml = stage_ml;
+  p.stage_o = stage_o;
+  p.R = s->num_requests;
+  p.BW = s->beam_width;
+  p.Hq = s->num_q_heads;
+  p.Hkv = s->num_kv_heads;
+  p.D = s->head_dim;
+  p.Lmax = s->max_prompt_len;
+  p.S = s->max_steps;
+  p.step = step;
+  p.G = p.Hq / p.Hkv;
+  p.M = p.BW * p.G;
+  p.scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)p.D);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
+  p.anc = nullptr;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (need > 0) {
+    int32_t *anc = static_cast<int32_t *>(workspace);
+    const xattn::AncLayout lay{(int64_t)(step + 1) * p.BW, 1, p.BW};  // [R][step+1][BW]
+    e = xattn::launch_resolve_ancestors(parent_idx, p.R, p.BW, p.S, step, anc, lay, hs);
+    if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+    p.anc = anc;
+  }
+  if (s->dtype == XATTN_F32)
+    e = xattn::launch_decode_f32(p, hs);
+  else
+    e = xattn::launch_decode_bf16(p, taps, hs);
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *shared_k,
+                          const void *shared_v, const int32_t *prompt_len,
+                          const void *unshared_k, const void *unshared_v,
+                          const int32_t *parent_idx, int32_t step, void *out, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream);
+}
+
+xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const void *shared_k,
+                                const void *shared_v, const int32_t *prompt_len,
+                                const void *unshared_k, const void *unshared_v,
+                                const int32_t *parent_idx, int32_t step, void *out, float *lse,
+                                float *stage_ml, float *stage_o, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+             out, lse, stage_ml, stage_o, true, workspace, workspace_bytes, stream);
+}
+
+size_t xattn_workspace_size(const xattn_shape *shape, int32_t step) {
+  if (check_shape(shape, step) != XATTN_OK) return (size_t)-1;
+  return workspace_bytes_for(shape, step);
+}
+
+xattn_status xattn_resolve_ancestors(const xattn_shape *shape, const int32_t *parent_idx,
+                                     int32_t step, int32_t *anc, void *stream) {
+  xattn_status st = check_shape(shape, step);
+  if (st != XATTN_OK) return st;
+  if (!parent_idx || !anc) return fail(XATTN_EINVAL, "a required pointer is NULL");
+  if (!aligned(parent_idx, 4) || !aligned(anc, 4))
+    return fail(XATTN_EINVAL, "int32 arrays must be 4-byte aligned");
+  const int32_t BW = shape->beam_width;
+  const xattn::AncLayout lay{(int64_t)BW * (step + 1), step + 1, 1};  // [R][BW][step+1]
+  hipError_t e = xattn::launch_resolve_ancestors(parent_idx, shape->num_requests, BW,
+                                                 shape->max_steps, step, anc, lay,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
+const char *xattn_status_string(xattn_status status) {
+  switch (status) {
+    case XATTN_OK: return "ok";
+    case XATTN_EINVAL: return "invalid argument";
+    case XATTN_EUNSUPPORTED: return "unsupported shape or dtype";
+    case XATTN_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *xattn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

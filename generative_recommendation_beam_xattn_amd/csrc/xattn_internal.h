@@ -1,0 +1,51 @@
+// Internal declarations of libxattn.so (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xattn {
+
+// Chains of at most this many levels are walked inside the attention kernel
+// (slots kept in LDS); deeper chains are resolved by the ancestor kernel into
+// the workspace first.
+constexpr int kMaxInKernelLevels = 16;
+
+// Everything a decode launch needs; passed by value as a kernel argument.
+struct DecodeParams {
+  const void *q;
+  const void *shared_k;
+  const void *shared_v;
+  const int32_t *prompt_len;
+  const void *unshared_k;
+  const void *unshared_v;
+  const int32_t *parent_idx;
+  void *out;
+  const int32_t *anc;  // [R][step+1][BW] resolved slots, or nullptr: walk in-kernel
+  float *lse;          // optional taps (debug entry only)
+  float *stage_ml;
+  float *stage_o;
+  int32_t R, BW, Hq, Hkv, D, Lmax, S, step;
+  int32_t G;           // Hq / Hkv, query heads per KV head
+  int32_t M;           // BW * G query rows per (request, KV head)
+  int32_t n_rb;        // row blocks per (request, KV head)
+  float scale;         // softmax scale
+  float scale_log2;    // scale * log2(e): scores go through exp2
+};
+
+// Ancestor output layouts: element (r, b, t) lives at
+//   r * stride_r + b * stride_b + t * stride_t.
+struct AncLayout {
+  int64_t stride_r, stride_b, stride_t;
+};
+
+hipError_t launch_resolve_ancestors(const int32_t *parent_idx, int32_t R, int32_t BW, int32_t S,
+                                    int32_t step, int32_t *anc, AncLayout layout,
+                                    hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream);
+
+// Number of query rows one bf16 workgroup owns for this shape.
+int bf16_rows_per_block(const DecodeParams &p);
+
+}  // namespace xattn

@@ -1,0 +1,148 @@
+/*
+ * xattn.h -- C ABI of libxattn.so: staged decode attention for beam-search
+ * generative recommendation on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the xAttention operator of the xGR technical summary
+ * (gist.science, paper 2512.11529), section 2.1:
+ *   - the KV cache is split into a Shared part, holding the prompt (user
+ *     history) K/V computed once at prefill and stored once per request, and
+ *     an Unshared part holding only the K/V of tokens generated during
+ *     decode, one row per (level, beam slot) with no block alignment;
+ *   - when beams branch nothing is copied: a beam reaches its generated
+ *     tokens through the per-step parent-slot indices;
+ *   - attention runs in three stages: the Shared and Unshared stages each
+ *     produce local scores with max/sum statistics, and a Merging stage
+ *     combines them with OnlineSoftmax.
+ * Because the merge is exact, for query head h of beam b in request r the
+ * result equals softmax attention over the concatenated keys
+ *     [ shared rows 0..L_r-1 of KV head k ; the beam's ancestor token at
+ *       every level 0..step of KV head k ],   k = h / (Hq / Hkv),
+ * scaled by `scale` (default 1/sqrt(D)).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers to caller-owned, dense,
+ *     row-major memory with the strides implied by the shape; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - q, K, V and out share one element type (xattn_dtype).  Their base
+ *     pointers must be 16-byte aligned; int32 arrays 4-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  Inputs must stay unchanged, and outputs are valid, only once
+ *     the stream has reached the enqueued work.
+ *   - Errors are status codes.  Every argument the host can check is checked
+ *     before anything is enqueued (XATTN_EINVAL / XATTN_EUNSUPPORTED); a HIP
+ *     launch failure returns XATTN_EHIP.  Nothing aborts, throws or prints;
+ *     xattn_last_error() gives a one-line reason for the calling thread.
+ *   - Values that live in device memory are preconditions, not checked:
+ *     0 <= prompt_len[r] <= max_prompt_len and 0 <= parent_idx < beam_width.
+ *     A violation gives unspecified output but no out-of-bounds access: the
+ *     kernels clamp both before forming addresses.
+ *   - Calls that share no output buffer may run concurrently.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  XATTN_OK = 0,
+  XATTN_EINVAL = 1,        /* an argument violates the contract below */
+  XATTN_EUNSUPPORTED = 2,  /* valid, but not a supported head_dim / dtype */
+  XATTN_EHIP = 3           /* the HIP runtime reported an error */
+} xattn_status;
+
+typedef enum {
+  XATTN_F32 = 0,   /* float32 inputs and output; fp32 arithmetic throughout */
+  XATTN_BF16 = 1   /* bfloat16 inputs and output; fp32 accumulation, output
+                      rounded to nearest even */
+} xattn_dtype;
+
+typedef struct {
+  int32_t num_requests;    /* R  >= 1 */
+  int32_t beam_width;      /* BW >= 1: beam slots per level */
+  int32_t num_q_heads;     /* Hq >= 1, a multiple of num_kv_heads */
+  int32_t num_kv_heads;    /* Hkv >= 1 */
+  int32_t head_dim;        /* D: 64 or 128 */
+  int32_t max_prompt_len;  /* Lmax >= 0: row capacity of the shared cache */
+  int32_t max_steps;       /* S >= 1: level capacity of the unshared cache */
+  int32_t dtype;           /* an xattn_dtype */
+  float scale;             /* softmax scale, finite and >= 0; 0 selects 1/sqrt(D) */
+} xattn_shape;
+
+/*
+ * One decode step of staged attention (the operation described above).
+ *
+ *   q           [R][BW][Hq][D]        query of every beam and head at `step`
+ *   shared_k/v  [R][Hkv][Lmax][D]     prompt K/V; rows < prompt_len[r] are read
+ *   prompt_len  [R] int32             L_r
+ *   unshared_k/v[R][Hkv][S][BW][D]    generated-token K/V, one row per (level,
+ *                                     slot); levels 0..step are read, so the
+ *                                     caller writes level `step` first
+ *   parent_idx  [R][S][BW] int32      parent_idx[r][t][b] = slot at level t-1
+ *                                     that the level-t beam in slot b extends;
+ *                                     rows 1..step are read, row 0 never
+ *   step        0 <= step < S         current level s
+ *   out         [R][BW][Hq][D]        written, same dtype as q
+ *   workspace   device scratch of at least xattn_workspace_size(shape, step)
+ *               bytes, 256-byte aligned; may be NULL when that size is 0.
+ *               Its contents on entry are ignored; two calls in flight at
+ *               once must not share one workspace.
+ */
+xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *shared_k,
+                          const void *shared_v, const int32_t *prompt_len,
+                          const void *unshared_k, const void *unshared_v,
+                          const int32_t *parent_idx, int32_t step, void *out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace xattn_decode / xattn_decode_debug need for this
+ * shape and step (0 if none).  Returns (size_t)-1 if the shape or step is
+ * invalid. */
+size_t xattn_workspace_size(const xattn_shape *shape, int32_t step);
+
+/*
+ * The ancestor slots a beam reaches through the parent chain, as used by the
+ * Unshared stage (xGR summary, section 2.1: generated tokens are kept per
+ * token and reached without copies when beams branch).
+ *   anc [R][BW][step+1] int32, written: anc[r][b][step] = b and
+ *   anc[r][b][t-1] = parent_idx[r][t][anc[r][b][t]] for t = step..1.
+ * Runs the same device code xattn_decode uses for deep chains.
+ */
+xattn_status xattn_resolve_ancestors(const xattn_shape *shape, const int32_t *parent_idx,
+                                     int32_t step, int32_t *anc, void *stream);
+
+/*
+ * xattn_decode that also exposes the stages (xGR summary, section 2.1: the
+ * Shared and Unshared stages each produce max/sum statistics, and the
+ * Merging stage combines them).  In this variant the two stages are
+ * computed separately and merged explicitly; out matches xattn_decode's to
+ * within rounding.  Every tap is optional (NULL skips it):
+ *   lse       [R][BW][Hq] float32     m + ln(sum), the merged log-normaliser
+ *   stage_ml  [2][R][BW][Hq][2] f32   (m, l) per stage: stage 0 Shared,
+ *                                     stage 1 Unshared; m = max scaled score,
+ *                                     l = sum exp(score - m).  An empty
+ *                                     prompt gives m = -inf, l = 0.
+ *   stage_o   [2][R][BW][Hq][D] f32   per-stage normalised output
+ *                                     (0 for an empty prompt)
+ */
+xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const void *shared_k,
+                                const void *shared_v, const int32_t *prompt_len,
+                                const void *unshared_k, const void *unshared_v,
+                                const int32_t *parent_idx, int32_t step, void *out,
+                                float *lse, float *stage_ml, float *stage_o, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *xattn_status_string(xattn_status status);
+
+/* Reason for the calling thread's most recent non-OK status ("" if none). */
+const char *xattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

@@ -1,0 +1,56 @@
+"""Host <-> device helpers for the GPU tests (marshalling only)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from generative_recommendation_beam_xattn_amd.workloads import bf16_bits_to_f32
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}   # max abs error vs the float64 oracle
+
+
+def to_dev(a: np.ndarray, device="cuda"):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def to_f64(t) -> np.ndarray:
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+class DeviceWorkload:
+    """A workload's arrays on the GPU (one copy; q per step)."""
+
+    def __init__(self, w, device="cuda"):
+        self.w = w
+        self.q = [to_dev(w.q[i], device) for i in range(len(w.steps))]
+        self.shared_k = to_dev(w.shared_k, device)
+        self.shared_v = to_dev(w.shared_v, device)
+        self.prompt_len = to_dev(w.prompt_len, device)
+        self.unshared_k = to_dev(w.unshared_k, device)
+        self.unshared_v = to_dev(w.unshared_v, device)
+        self.parent_idx = to_dev(w.parent_idx, device)
+
+    def args(self, i):
+        return (self.q[i], self.shared_k, self.shared_v, self.prompt_len, self.unshared_k,
+                self.unshared_v, self.parent_idx, self.w.steps[i])
+
+
+def host_args(w, i):
+    return (w.q[i], w.shared_k, w.shared_v, w.prompt_len, w.unshared_k, w.unshared_v,
+            w.parent_idx, w.steps[i])
+
+
+def sample_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.stack([rng.integers(0, w.R, n), rng.integers(0, w.BW, n), rng.integers(0, w.Hq, n)],
+                    axis=1).astype(np.int32)
+    # always include the corners
+    corners = np.array([[0, 0, 0], [w.R - 1, w.BW - 1, w.Hq - 1], [0, w.BW - 1, 0],
+                        [w.R - 1, 0, w.Hq - 1]], np.int32)
+    return np.concatenate([corners, rows])

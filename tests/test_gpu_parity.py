@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bars: max abs error <= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs
+(fp32 accumulation, bf16 output); ancestor slots bit-exact.  Small shapes
+span several 64-key tiles, ragged tails of keys and query rows, every tiling
+the launcher picks, deep parent chains and the degenerate cases; the full
+workload sizes are checked on sampled rows the oracle computes one by one,
+in the launch configuration the benchmark times.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import generative_recommendation_beam_xattn_amd as X
+from generative_recommendation_beam_xattn_amd import workloads as W
+from tests.gpu_util import TOL, DeviceWorkload, host_args, sample_rows, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def check_full(w, name):
+    dw = DeviceWorkload(w)
+    for i, s in enumerate(w.steps):
+        say("[%s] decode step %d (R=%d BW=%d Hq=%d Hkv=%d D=%d S=%d %s)" % (
+            name, s, w.R, w.BW, w.Hq, w.Hkv, w.D, w.S, w.dtype))
+        out = X.decode(*dw.args(i))
+        torch.cuda.synchronize()
+        ref, _ = oracle.attend(*host_args(w, i))
+        err = np.max(np.abs(to_f64(out) - ref))
+        assert err <= TOL[w.dtype], "%s step %d: max abs err %g" % (name, s, err)
+
+
+SMALL = {
+    # name: workload kwargs
+    "ragged_rows_1wave": dict(R=3, BW=5, Hq=8, Hkv=2, D=128, L=[0, 77, 200], steps=[0, 1, 2]),
+    "two_rowblocks_4x1": dict(R=2, BW=40, Hq=8, Hkv=2, D=128, L=[129, 511], steps=[0, 2], S=3),
+    "d64_2waves": dict(R=2, BW=17, Hq=6, Hkv=3, D=64, L=[64, 191], steps=[1]),
+    "g1_4x1": dict(R=2, BW=70, Hq=2, Hkv=2, D=128, L=[300, 1], steps=[2]),
+    "qb2_tiling": dict(R=64, BW=64, Hq=32, Hkv=8, D=128, L=(30, 150), steps=[1], S=2),
+    "deep_chain_workspace": dict(R=2, BW=6, Hq=4, Hkv=2, D=128, L=[50, 0], steps=[39], S=40),
+    "deep_chain_wide": dict(R=1, BW=300, Hq=4, Hkv=4, D=64, L=[65], steps=[20], S=24),
+    "single_beam_empty_prompt": dict(R=2, BW=1, Hq=4, Hkv=1, D=128, L=[0, 0], steps=[0]),
+    "no_shared_rows": dict(R=2, BW=3, Hq=4, Hkv=2, D=64, L=[0, 0], steps=[1], Lmax=0),
+}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_shapes(name, dtype):
+    kw = dict(SMALL[name])
+    w = W.custom(name=name, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, **kw)
+    check_full(w, name + "/" + dtype)
+
+
+def test_tiny_workload_all_steps():
+    w = W.make(1)
+    check_full(w, "tiny")
+
+
+@pytest.mark.parametrize("config", [2, 3, 4])
+def test_full_size_sampled(config):
+    w = W.make(config)
+    dw = DeviceWorkload(w)
+    for i, s in enumerate(w.steps):
+        say("[config %d] decode step %d sampled" % (config, s))
+        out = X.decode(*dw.args(i))
+        torch.cuda.synchronize()
+        rows = sample_rows(w, 512, seed=100 + s)
+        ref, _ = oracle.attend(*host_args(w, i), rows=rows)
+        got = to_f64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
+        err = np.max(np.abs(got - ref))
+        assert err <= TOL["bf16"], "config %d step %d: %g" % (config, s, err)
+        assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("G", W.PREFIX_GROUPS)
+def test_prefix_sweep_sampled(G):
+    w = W.make(5, G)
+    dw = DeviceWorkload(w)
+    say("[prefix sweep G=%d] decode step %d sampled" % (G, w.steps[0]))
+    out = X.decode(*dw.args(0))
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 256, seed=G)
+    ref, _ = oracle.attend(*host_args(w, 0), rows=rows)
+    got = to_f64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.max(np.abs(got - ref)) <= TOL["bf16"]
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4])
+def test_ancestors_exact(config):
+    w = W.make(config)
+    par = to_dev(w.parent_idx)
+    for s in w.steps:
+        say("[config %d] resolve_ancestors step %d" % (config, s))
+        anc = X.resolve_ancestors(par, s).cpu().numpy()
+        assert np.array_equal(anc, oracle.ancestors(w.parent_idx, s))
+
+
+@pytest.mark.parametrize("BW,S,step", [(1, 512, 511), (256, 512, 511), (7, 33, 32), (9000, 3, 2),
+                                       (300, 64, 0)])
+def test_ancestors_exact_random_chains(BW, S, step):
+    rng = np.random.default_rng(BW + S)
+    p = rng.integers(0, BW, size=(2, S, BW), dtype=np.int32)
+    say("[ancestors] BW=%d S=%d step=%d" % (BW, S, step))
+    anc = X.resolve_ancestors(to_dev(p), step).cpu().numpy()
+    assert np.array_equal(anc, oracle.ancestors(p, step))
+
+
+DEBUG = {
+    "tiny": None,
+    "bf16_ragged": dict(R=3, BW=5, Hq=8, Hkv=2, D=128, L=[0, 77, 200], steps=[2]),
+    "bf16_rowblocks": dict(R=2, BW=40, Hq=8, Hkv=2, D=64, L=[129, 64], steps=[1]),
+    "bf16_deep": dict(R=2, BW=6, Hq=4, Hkv=2, D=128, L=[50, 0], steps=[39], S=40),
+    "f32_ragged": dict(R=2, BW=5, Hq=8, Hkv=2, D=128, L=[0, 130], steps=[2], dtype="f32"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DEBUG))
+def test_debug_stage_taps(name):
+    w = W.make(1) if DEBUG[name] is None else W.custom(name=name, seed=7, **DEBUG[name])
+    dw = DeviceWorkload(w)
+    i = len(w.steps) - 1
+    say("[debug %s] decode_debug step %d" % (name, w.steps[i]))
+    out, lse, ml, o = X.decode_debug(*dw.args(i))
+    out_fast = X.decode(*dw.args(i))
+    torch.cuda.synchronize()
+    tol = TOL[w.dtype]
+    ref, ref_lse = oracle.attend(*host_args(w, i))
+    part = oracle.stage_partials(*host_args(w, i))
+    assert np.max(np.abs(to_f64(out) - ref)) <= tol
+    assert np.max(np.abs(to_f64(out_fast) - ref)) <= tol
+    assert np.max(np.abs(lse.cpu().numpy() - ref_lse)) <= tol
+    ml = ml.cpu().numpy().astype(np.float64)
+    o = o.cpu().numpy().astype(np.float64)
+    for s_idx, key in ((0, "shared"), (1, "unshared")):
+        rml, ro = part[key + "_ml"], part[key + "_o"]
+        empty = rml[..., 1] == 0
+        assert np.array_equal(ml[s_idx][..., 1] == 0, empty)
+        assert np.all(np.isneginf(ml[s_idx][..., 0][empty]))
+        ne = ~empty
+        assert np.max(np.abs(ml[s_idx][..., 0][ne] - rml[..., 0][ne]), initial=0) <= tol
+        # l is a sum of exp terms, compare relatively
+        rel = np.abs(ml[s_idx][..., 1][ne] - rml[..., 1][ne]) / rml[..., 1][ne]
+        assert np.max(rel, initial=0) <= tol
+        assert np.max(np.abs(o[s_idx] - ro)) <= tol
+
+
+def test_never_reads_past_prompt_step_or_row_zero():
+    w = W.custom(name="poison", seed=3, R=3, BW=6, Hq=8, Hkv=2, D=128, L=[5, 70, 0], steps=[1],
+                 S=4, Lmax=96)
+    ref, _ = oracle.attend(*host_args(w, 0))
+    nan = np.uint16(0x7FC0)
+    for a in (w.shared_k, w.shared_v):
+        for r, L in enumerate(w.prompt_len):
+            a[r, :, L:] = nan
+    for a in (w.unshared_k, w.unshared_v):
+        a[:, :, 2:] = nan
+    w.parent_idx[:, 0] = 3      # row 0 is never followed
+    dw = DeviceWorkload(w)
+    say("[poison] decode step 1")
+    out = X.decode(*dw.args(0))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    assert np.max(np.abs(to_f64(out) - ref)) <= TOL["bf16"]
+
+
+def test_bitwise_deterministic_and_out_buffer_reuse():
+    w = W.make(2, R=4)
+    dw = DeviceWorkload(w)
+    say("[determinism] config 2 (4 requests)")
+    a = X.decode(*dw.args(1))
+    out = torch.full_like(a, float("nan"))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        X.decode(*dw.args(1), out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), out.view(torch.int16))
+
+
+def test_invalid_arguments_raise_before_launch():
+    w = W.custom(name="inv", seed=1, R=1, BW=2, Hq=2, Hkv=1, D=128, L=[8], steps=[0], S=2)
+    dw = DeviceWorkload(w)
+    q, sk, sv, pl, uk, uv, par, _ = dw.args(0)
+    with pytest.raises(X.XattnError) as e:
+        X.decode(q, sk, sv, pl, uk, uv, par, 2)
+    assert e.value.status == 1
+    with pytest.raises(X.XattnError) as e:
+        X.decode(q[..., :96].contiguous(), sk[..., :96].contiguous(), sv[..., :96].contiguous(),
+                 pl, uk[..., :96].contiguous(), uv[..., :96].contiguous(), par, 0)
+    assert e.value.status == 2
