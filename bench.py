@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of staged beam-search decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--G g]
+
+One benchmark step is one pass of the whole path over one batch of the
+workload: for the default GR-serving workload (16 requests, prompt lengths
+uniform in [512, 1024], 128 beams, 3 decode steps, 16 query / 4 KV heads,
+head_dim 128, bf16) that is 3 calls of xattn_decode, levels 0, 1, 2.  Inputs
+are resident in HBM before timing starts; enough distinct copies of them are
+rotated (>= 1 GB) that timed calls read HBM rather than the 256 MB Infinity
+Cache.
+
+Prints ONE JSON line.  `value` is beam-steps per second over the timed
+region (wall clock between two device synchronisations).  `roofline` covers
+the decode kernel: algorithmic bytes (unique KV rows + q + out + indices) or
+FLOPs per launch divided by the kernel's mean launch duration, measured with
+HIP events on the launch stream.  `cpu_baseline` times the float64 CPU
+oracle on the host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention beam-steps/sec + achieved HBM GB/s (unique KV bytes) vs peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+KERNEL_SOURCES = {"bf16": "generative_recommendation_beam_xattn_amd/csrc/kernel_bf16_mfma.hip",
+                  "f32": "generative_recommendation_beam_xattn_amd/csrc/kernel_f32.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--G", type=int, default=None, help="prefix group size for config 5")
+    ap.add_argument("--rot", type=int, default=None, help="rotation copies (default: >= 1 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- accounting
+
+def distinct_ancestor_rows(parent_idx_r: np.ndarray, step: int) -> int:
+    """Sum over levels 0..step of the number of distinct slots any beam reaches."""
+    BW = parent_idx_r.shape[1]
+    live = np.arange(BW)
+    total = 0
+    for t in range(step, -1, -1):
+        live = np.unique(live)
+        total += live.size
+        if t >= 1:
+            live = parent_idx_r[t][live]
+    return total
+
+
+def algorithmic_work(w, step_index: int) -> dict:
+    """Compulsory bytes and FLOPs of one xattn_decode call."""
+    s = w.steps[step_index]
+    e = w.elem_bytes
+    row_bytes = w.D * e
+    shared_rows = int(np.sum(w.prompt_len)) * w.Hkv
+    unshared_rows = sum(distinct_ancestor_rows(w.parent_idx[r], s) for r in range(w.R)) * w.Hkv
+    kv_bytes = 2 * row_bytes * (shared_rows + unshared_rows)   # K and V
+    q_bytes = w.R * w.BW * w.Hq * row_bytes
+    idx_bytes = w.R * s * w.BW * 4 + w.R * 4
+    G = w.Hq // w.Hkv
+    flops = 4 * w.D * G * w.BW * w.Hkv * int(np.sum(w.prompt_len.astype(np.int64) + s + 1))
+    return {"unique_kv_bytes": kv_bytes, "q_out_bytes": 2 * q_bytes, "index_bytes": idx_bytes,
+            "bytes": kv_bytes + 2 * q_bytes + idx_bytes, "flops": flops}
+
+
+def workload_config(w, n_rot: int) -> dict:
+    c = {"workload": w.name, "requests": w.R, "beam_width": w.BW, "q_heads": w.Hq,
+         "kv_heads": w.Hkv, "head_dim": w.D, "decode_steps": list(w.steps),
+         "calls_per_step": len(w.steps), "rotation_copies": n_rot}
+    lo, hi = int(w.prompt_len.min()), int(w.prompt_len.max())
+    c["prompt_len"] = lo if lo == hi else "uniform [%d, %d] (drawn %d..%d)" % (
+        {2: 512}.get(w.meta.get("config"), lo), {2: 1024}.get(w.meta.get("config"), hi), lo, hi)
+    if w.meta.get("G"):
+        c["prefix_group"] = w.meta["G"]
+    return c
+
+
+def kernel_digest(dtype: str) -> str:
+    with open(os.path.join(ROOT, KERNEL_SOURCES[dtype]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(w, dtype: str):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha256_16") != kernel_digest(dtype):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+def cpu_baseline(w, target_s: float) -> dict:
+    """Float64 oracle throughput on this host, over whole passes of the workload
+    ((request, decode step) pairs in order, repeated) until ~target_s of CPU time."""
+    import oracle
+    t_total, beam_steps, n_pairs = 0.0, 0, 0
+    order = [(r, i) for r in range(w.R) for i in range(len(w.steps))]
+    while t_total < target_s:
+        for r, i in order:
+            sl = slice(r, r + 1)
+            t0 = time.perf_counter()
+            oracle.attend(w.q[i][sl], w.shared_k[sl], w.shared_v[sl], w.prompt_len[sl],
+                          w.unshared_k[sl], w.unshared_v[sl], w.parent_idx[sl], w.steps[i])
+            t_total += time.perf_counter() - t0
+            beam_steps += w.BW
+            n_pairs += 1
+            if t_total >= target_s:
+                break
+    return {"value": beam_steps / t_total, "unit": "beam-steps/s", "cores": oracle.omp_threads(),
+            "kind": "oracle",
+            "sample": "%d (request, decode step) pairs of the %s workload (%d per full pass), %d "
+                      "beams each, %.1f s of float64 oracle time" % (
+                          n_pairs, w.name, len(order), w.BW, t_total)}
+
+
+# ---------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported.  The path shards "
+              "by request or KV head with no exchange, so N GPUs would each run this kernel on "
+              "their share." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from generative_recommendation_beam_xattn_amd import binding as B
+    from generative_recommendation_beam_xattn_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    w = W.make(args.config, args.G)
+    n_calls = len(w.steps)
+    work = [algorithmic_work(w, i) for i in range(n_calls)]
+    copy_bytes = (w.q.nbytes * 2 + w.shared_k.nbytes * 2 + w.unshared_k.nbytes * 2 +
+                  w.parent_idx.nbytes)
+    n_rot = args.rot or max(1, min(32, math.ceil(1e9 / copy_bytes)))
+
+    # rotation copies of every input (and output) resident in HBM
+    base = {"q": [to_dev(w.q[i]) for i in range(n_calls)], "sk": to_dev(w.shared_k),
+            "sv": to_dev(w.shared_v), "pl": to_dev(w.prompt_len), "uk": to_dev(w.unshared_k),
+            "uv": to_dev(w.unshared_v), "par": to_dev(w.parent_idx)}
+    copies = [base] + [{k: ([t.clone() for t in v] if isinstance(v, list) else v.clone())
+                        for k, v in base.items()} for _ in range(n_rot - 1)]
+    calls = [[B.PreparedDecode(c["q"][i], c["sk"], c["sv"], c["pl"], c["uk"], c["uv"], c["par"],
+                               w.steps[i]) for i in range(n_calls)] for c in copies]
+    stream = torch.cuda.current_stream(dev)
+
+    def run_step(k, events=None):
+        for i, call in enumerate(calls[k % n_rot]):
+            if events is not None:
+                events[2 * i].record(stream)
+            call(stream)
+            if events is not None:
+                events[2 * i + 1].record(stream)
+
+    for k in range(args.warmup):
+        run_step(k)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        run_step(args.warmup + k, ev[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    # per-launch durations (ms) of each decode call, by level
+    per_call = np.array([[ev[k][2 * i].elapsed_time(ev[k][2 * i + 1]) for i in range(n_calls)]
+                         for k in range(args.steps)])
+    mean_launch_s = per_call.mean(axis=0) / 1e3
+    t_kernel = float(mean_launch_s.mean())
+    bytes_per_launch = float(np.mean([x["bytes"] for x in work]))
+    flops_per_launch = float(np.mean([x["flops"] for x in work]))
+    ukv_per_launch = float(np.mean([x["unique_kv_bytes"] for x in work]))
+    t_hbm = bytes_per_launch / (HBM_PEAK_GBS * 1e9)
+    peak_c = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+    t_cmp = flops_per_launch / (peak_c * 1e12)
+    if t_hbm >= t_cmp:
+        achieved = bytes_per_launch / t_kernel / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        achieved = flops_per_launch / t_kernel / 1e12
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
+                "peak": peak_c, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(w, w.dtype)
+
+    beam_steps = args.steps * n_calls * w.R * w.BW
+    line = {
+        "metric": METRIC,
+        "value": beam_steps / wall,
+        "unit": "beam-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), workload shape of the GR serving configuration)",
+        "config": workload_config(w, n_rot),
+        "roofline": roof,
+        "unique_kv_GBps": ukv_per_launch / t_kernel / 1e9,
+        "unique_kv_frac_of_hbm_peak": ukv_per_launch / t_kernel / 1e9 / HBM_PEAK_GBS,
+        "binding_roofline_frac": max(t_hbm, t_cmp) / t_kernel,
+        "kernel_us_per_launch": {"mean": t_kernel * 1e6,
+                                 "by_level": [float(x * 1e6) for x in mean_launch_s],
+                                 "p10": float(np.percentile(per_call, 10) * 1e3),
+                                 "p50": float(np.percentile(per_call, 50) * 1e3),
+                                 "p90": float(np.percentile(per_call, 90) * 1e3)},
+        "algorithmic_per_launch": {"bytes": bytes_per_launch, "unique_kv_bytes": ukv_per_launch,
+                                   "flops": flops_per_launch},
+        "kernel_sha256_16": kernel_digest(w.dtype),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -205,3 +205,31 @@ def resolve_ancestors(parent_idx, step: int, stream=None):
     _check(lib.xattn_resolve_ancestors(ctypes.byref(shape), _ptr(parent_idx), int(step),
                                        _ptr(anc), _stream(stream, parent_idx.device)))
     return anc
+
+
+class PreparedDecode:
+    """xattn_decode with its arguments marshalled once (for tight loops).
+
+    Holds references to the tensors so their storage outlives the object;
+    ``__call__`` enqueues one decode step on ``stream`` (a torch stream, or
+    the current stream) and raises on a non-OK status.
+    """
+
+    def __init__(self, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx,
+                 step, out=None, workspace=None, scale: float = 0.0):
+        _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
+        self.lib = load()
+        self.shape = make_shape(q, shared_k, unshared_k, scale)
+        self.out = torch.empty_like(q) if out is None else out
+        self.ws, ws_bytes = _workspace(self.shape, step, workspace, q.device)
+        self._keep = (q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
+        self.device = q.device
+        self.args = (ctypes.byref(self.shape), _ptr(q), _ptr(shared_k), _ptr(shared_v),
+                     _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v), _ptr(parent_idx),
+                     int(step), _ptr(self.out), _ptr(self.ws), ws_bytes)
+
+    def __call__(self, stream=None):
+        st = self.lib.xattn_decode(*self.args, _stream(stream, self.device))
+        if st != XATTN_OK:
+            _check(st)
+        return self.out

@@ -81,38 +81,223 @@ __device__ inline int vt_pos(int key) {
 
 __device__ inline int clampi(int v, int lo, int hi) { return min(max(v, lo), hi); }
 
-template <int D, int WAVES, int QB, bool TAPS>
-__global__ __launch_bounds__(WAVES * 64) void decode_bf16_kernel(DecodeParams p) {
+// Both halves of the wave hold complementary parts of a row's statistics
+// (lane l and lane l ^ 32).  v_permlane32_swap exchanges the halves on the
+// VALU; combining the two results symmetrically gives every lane the pair's
+// max or sum.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin.  Giving each XCD a
+// contiguous range of logical blocks keeps the row blocks of one
+// (request, KV head) on one XCD, where they share its L2.
+__device__ inline int xcd_logical_block(int b, int n) {
+  const int xcd = b & 7, j = b >> 3;
+  const int per = n >> 3, extra = n & 7;
+  return xcd * per + min(xcd, extra) + j;
+}
+
+// A row's running maximum is only raised when a tile exceeds it by more
+// than 2^8 in the exp2 domain; until then p = exp2(s - m) may exceed 1 (by
+// at most 256), which fp32 sums and bf16 P hold without loss of range.
+constexpr float kLazyRescaleLog2 = 8.0f;
+
+// LDS layout of one workgroup: two K tiles [KT][D + KPAD] and two V^T tiles
+// [D][KT + VPAD] (double buffered).  After the last tile the same bytes hold
+// the partial states the key halves exchange.
+template <int D>
+struct TileLds {
+  static constexpr int kPitch = D + KPAD;
+  static constexpr int vPitch = KT + VPAD;
+  static constexpr int kBytes = KT * kPitch * 2;
+  static constexpr int vBytes = D * vPitch * 2;
+  static constexpr int bytes = 2 * (kBytes + vBytes);
+  __device__ static uint16_t *k(uint8_t *base, int buf) {
+    return reinterpret_cast<uint16_t *>(base + buf * kBytes);
+  }
+  __device__ static uint16_t *vt(uint8_t *base, int buf) {
+    return reinterpret_cast<uint16_t *>(base + 2 * kBytes + buf * vBytes);
+  }
+};
+
+// Staging registers of one thread for one shared K/V tile.  K is moved in
+// 16-byte chunks; V in blocks of 4 keys x 8 dims that are transposed in
+// registers on the way into the V^T tile.  With 8 waves, the lower half of
+// the workgroup moves K and the upper half moves V.
+template <int D, int NT>
+struct TileStage {
+  static constexpr bool kSplitRoles = NT >= 512;
+  static constexpr int kThreads = kSplitRoles ? NT / 2 : NT;
+  static constexpr int KCH = KT * D / 8;
+  static constexpr int VBL = KT * D / 32;
+  static constexpr int KPT = (KCH + kThreads - 1) / kThreads;
+  static constexpr int VPT = (VBL + kThreads - 1) / kThreads;
+  // one register file for both roles when they are split across threads
+  static constexpr int NREG = kSplitRoles ? (KPT > 4 * VPT ? KPT : 4 * VPT) : KPT + 4 * VPT;
+  static constexpr int VOFF = kSplitRoles ? 0 : KPT;
+  uint4 reg[NREG];
+  __device__ uint4 &k(int i) { return reg[i]; }
+  __device__ uint4 &v(int i, int e) { return reg[VOFF + 4 * i + e]; }
+  __device__ const uint4 &k(int i) const { return reg[i]; }
+  __device__ const uint4 &v(int i, int e) const { return reg[VOFF + 4 * i + e]; }
+};
+
+template <int D, int NT>
+__device__ __forceinline__ void tile_load(TileStage<D, NT> &st, int tid, const uint16_t *skg,
+                                          const uint16_t *svg, int key0, int L) {
+  using S = TileStage<D, NT>;
+  // Rows past the prompt are clamped to its last row (always in bounds):
+  // their scores are masked and their probabilities are exactly zero.
+  const bool do_k = !S::kSplitRoles || tid < S::kThreads;
+  const bool do_v = !S::kSplitRoles || tid >= S::kThreads;
+  const int t = S::kSplitRoles ? tid % S::kThreads : tid;
+  if (do_k) {
+#pragma unroll
+    for (int i = 0; i < S::KPT; ++i) {
+      const int ch = t + i * S::kThreads;
+      if (S::KCH % S::kThreads == 0 || ch < S::KCH) {
+        const int key = min(key0 + ch / (D / 8), L - 1);
+        st.k(i) = *reinterpret_cast<const uint4 *>(skg + (int64_t)key * D + (ch % (D / 8)) * 8);
+      }
+    }
+  }
+  if (do_v) {
+#pragma unroll
+    for (int i = 0; i < S::VPT; ++i) {
+      const int bl = t + i * S::kThreads;
+      if (S::VBL % S::kThreads == 0 || bl < S::VBL) {
+        const int dc = bl % (D / 8);
+        const int key = key0 + 4 * (bl / (D / 8));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          st.v(i, e) = *reinterpret_cast<const uint4 *>(
+              svg + (int64_t)min(key + e, L - 1) * D + dc * 8);
+      }
+    }
+  }
+}
+
+template <int D, int NT>
+__device__ __forceinline__ void tile_store(const TileStage<D, NT> &st, int tid, uint8_t *lds,
+                                           int buf) {
+  using S = TileStage<D, NT>;
+  using T = TileLds<D>;
+  const bool do_k = !S::kSplitRoles || tid < S::kThreads;
+  const bool do_v = !S::kSplitRoles || tid >= S::kThreads;
+  const int t = S::kSplitRoles ? tid % S::kThreads : tid;
+  uint16_t *kl = T::k(lds, buf);
+  uint16_t *vl = T::vt(lds, buf);
+  if (do_k) {
+#pragma unroll
+    for (int i = 0; i < S::KPT; ++i) {
+      const int ch = t + i * S::kThreads;
+      if (S::KCH % S::kThreads == 0 || ch < S::KCH)
+        *reinterpret_cast<uint4 *>(kl + (ch / (D / 8)) * T::kPitch + (ch % (D / 8)) * 8) =
+            st.k(i);
+    }
+  }
+  if (do_v) {
+#pragma unroll
+    for (int i = 0; i < S::VPT; ++i) {
+      const int bl = t + i * S::kThreads;
+      if (S::VBL % S::kThreads == 0 || bl < S::VBL) {
+        const int dc = bl % (D / 8);
+        const int pos = vt_pos(4 * (bl / (D / 8)));
+        const uint4 r0 = st.v(i, 0), r1 = st.v(i, 1), r2 = st.v(i, 2), r3 = st.v(i, 3);
+        const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+        const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+        const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
+        const uint32_t w3[4] = {r3.x, r3.y, r3.z, r3.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // dims 2e and 2e+1 of the four keys
+          const uint2 even = {(w0[e] & 0xffffu) | (w1[e] << 16), (w2[e] & 0xffffu) | (w3[e] << 16)};
+          const uint2 odd = {(w0[e] >> 16) | (w1[e] & 0xffff0000u),
+                             (w2[e] >> 16) | (w3[e] & 0xffff0000u)};
+          *reinterpret_cast<uint2 *>(vl + (dc * 8 + 2 * e) * T::vPitch + pos) = even;
+          *reinterpret_cast<uint2 *>(vl + (dc * 8 + 2 * e + 1) * T::vPitch + pos) = odd;
+        }
+      }
+    }
+  }
+}
+
+// Workgroup = RG row groups x KSPLIT key halves, one wave each.  A row group
+// owns QB blocks of 32 query rows; with KSPLIT = 2 the two waves of a row
+// group take the two 32-key halves of every 64-key tile and merge their
+// online-softmax states through LDS at the end.
+template <int D, int RG, int QB, int KSPLIT, bool TAPS>
+__global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodeParams p) {
+  constexpr int WAVES = RG * KSPLIT;
   constexpr int NT = WAVES * 64;
-  constexpr int ROWS = WAVES * QB * 32;
+  constexpr int ROWS = RG * QB * 32;
   constexpr int NKS = D / 16;           // k-steps of the QK contraction
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  constexpr int KCH = KT * D / 8;       // 16-byte K chunks per tile
-  constexpr int KPT = (KCH + NT - 1) / NT;
-  constexpr int VBL = KT * D / 32;      // (4 keys x 8 dims) V blocks per tile
-  constexpr int VPT = (VBL + NT - 1) / NT;
+  constexpr int NKB = 2 / KSPLIT;       // 32-key blocks per wave per tile
+  using T = TileLds<D>;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT][D + KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D][KT + VPAD];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[T::bytes];
   extern __shared__ int32_t anc_lds[];  // [beams of the block][step + 1]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hl = lane >> 5;   // lane half
-  const int ql = lane & 31;   // query (B/C column) or A-operand row of this lane
+  const int rg = wave % RG;     // row group
+  const int kh = wave / RG;     // key half
+  const int hl = lane >> 5;     // lane half
+  const int ql = lane & 31;     // query (B/C column) or A-operand row of this lane
 
-  const int rb = blockIdx.x % p.n_rb;
-  const int unit = blockIdx.x / p.n_rb;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int rb = lb % p.n_rb;
+  const int unit = lb / p.n_rb;
   const int r = unit / p.Hkv;
   const int k = unit % p.Hkv;
   const int G = p.G, BW = p.BW, step = p.step;
   const int L = clampi(p.prompt_len[r], 0, p.Lmax);
   const float c = p.scale_log2;
+  // in raw dot-product units; the debug variant reports the stages' true
+  // maxima, so it raises m on every increase
+  const float thr = TAPS ? 0.f : kLazyRescaleLog2 / c;
 
   const int row0 = rb * ROWS;
   const int b_lo = row0 / G;
   const int nb = min(BW - b_lo, (ROWS - 1) / G + 2);
+  const int n_tiles = (L + KT - 1) / KT;
+
+  // ---- loads that depend on nothing: q rows, shared tile 0
+  const uint16_t *qg = static_cast<const uint16_t *>(p.q);
+  uint16_t *og = static_cast<uint16_t *>(p.out);
+  bf16x8 qf[QB][NKS];
+  int beam[QB];
+  int64_t qoff[QB];
+  bool valid[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = row0 + (rg * QB + qb) * 32 + ql;
+    valid[qb] = row < p.M;
+    const int rr = valid[qb] ? row : p.M - 1;
+    beam[qb] = rr / G;
+    const int h = k * G + rr % G;
+    qoff[qb] = (((int64_t)r * BW + beam[qb]) * p.Hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                  qg + qoff[qb] + ks * 16 + hl * 8));
+  }
+  const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  const uint16_t *svg = static_cast<const uint16_t *>(p.shared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  TileStage<D, NT> stage;
+  if (n_tiles > 0) tile_load<D, NT>(stage, tid, skg, svg, 0, L);
 
   // ---- ancestor slots of the block's beams (short chains: walked here)
   if (p.anc == nullptr) {
@@ -127,34 +312,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_bf16_kernel(DecodeParams p)
       }
     }
   }
+  if (n_tiles > 0) tile_store<D, NT>(stage, tid, lds, 0);
+  __syncthreads();  // ancestor slots and tile 0 visible
+  if (n_tiles > 1) tile_load<D, NT>(stage, tid, skg, svg, KT, L);
 
-  // ---- this lane's query rows
-  const uint16_t *qg = static_cast<const uint16_t *>(p.q);
-  uint16_t *og = static_cast<uint16_t *>(p.out);
-  bf16x8 qf[QB][NKS];
-  int beam[QB];
-  int64_t qoff[QB];
-  bool valid[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = row0 + (wave * QB + qb) * 32 + ql;
-    valid[qb] = row < p.M;
-    const int rr = valid[qb] ? row : p.M - 1;
-    beam[qb] = rr / G;
-    const int h = k * G + rr % G;
-    qoff[qb] = (((int64_t)r * BW + beam[qb]) * p.Hq + h) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                  qg + qoff[qb] + ks * 16 + hl * 8));
-  }
-  __syncthreads();  // ancestor slots visible
-
-  // ---- Unshared stage: the beam's token at every level 0..step
-  const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
-                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
-  const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
-                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  // ---- Unshared stage: the beam's token at every level.  The debug variant
+  // keeps it in key half 0; otherwise the key halves take alternate levels
+  // (their partial states are merged with the rest at the end).
   float m[QB], l[QB];
   f32x16 O[QB][NDB];
 #pragma unroll
@@ -163,32 +327,52 @@ __global__ __launch_bounds__(WAVES * 64) void decode_bf16_kernel(DecodeParams p)
     l[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) O[qb][db] = f32x16{};
-    const int bi = beam[qb] - b_lo;
-    for (int t = 0; t <= step; ++t) {
-      const int slot = p.anc ? clampi(p.anc[((int64_t)r * (step + 1) + t) * BW + beam[qb]], 0,
-                                      BW - 1)
-                             : anc_lds[bi * (step + 1) + t];
-      const int64_t roff = ((int64_t)t * BW + slot) * D;
-      float part = 0.f;
+  }
+  if (!TAPS || kh == 0) {
+    const int t_first = TAPS ? 0 : kh;
+    const int t_stride = TAPS ? 1 : KSPLIT;
+    const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
+                          ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+    const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
+                          ((int64_t)r * p.Hkv + k) * p.S * BW * D;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        part = dot8(__builtin_bit_cast(uint4, qf[qb][ks]),
-                    *reinterpret_cast<const uint4 *>(ukg + roff + ks * 16 + hl * 8), part);
-      const float sc = part + __shfl_xor(part, 32);
-      const float mn = fmaxf(m[qb], sc);
-      const float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c);
-      const float pr = __builtin_amdgcn_exp2f((sc - mn) * c);
-      l[qb] = l[qb] * alpha + pr;
-      m[qb] = mn;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int bi = beam[qb] - b_lo;
+      for (int t = t_first; t <= step; t += t_stride) {
+        const int slot = p.anc ? clampi(p.anc[((int64_t)r * (step + 1) + t) * BW + beam[qb]], 0,
+                                        BW - 1)
+                               : anc_lds[bi * (step + 1) + t];
+        const int64_t roff = ((int64_t)t * BW + slot) * D;
+        uint4 kr[NKS];
+        uint2 vr[NDB][4];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+        for (int ks = 0; ks < NKS; ++ks)
+          kr[ks] = *reinterpret_cast<const uint4 *>(ukg + roff + ks * 16 + hl * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint2 v = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
-          O[qb][db][4 * j + 0] = fmaf(O[qb][db][4 * j + 0], alpha, pr * lo_bf16(v.x));
-          O[qb][db][4 * j + 1] = fmaf(O[qb][db][4 * j + 1], alpha, pr * hi_bf16(v.x));
-          O[qb][db][4 * j + 2] = fmaf(O[qb][db][4 * j + 2], alpha, pr * lo_bf16(v.y));
-          O[qb][db][4 * j + 3] = fmaf(O[qb][db][4 * j + 3], alpha, pr * hi_bf16(v.y));
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            vr[db][j] = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
+        float part = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          part = dot8(__builtin_bit_cast(uint4, qf[qb][ks]), kr[ks], part);
+        const float sc = pair_sum(part);
+        const float mn = fmaxf(m[qb], sc);
+        const float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c);  // 0 while m is -inf
+        const float pr = __builtin_amdgcn_exp2f((sc - mn) * c);
+        l[qb] = l[qb] * alpha + pr;
+        m[qb] = mn;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint2 v = vr[db][j];
+            O[qb][db][4 * j + 0] = fmaf(O[qb][db][4 * j + 0], alpha, pr * lo_bf16(v.x));
+            O[qb][db][4 * j + 1] = fmaf(O[qb][db][4 * j + 1], alpha, pr * hi_bf16(v.x));
+            O[qb][db][4 * j + 2] = fmaf(O[qb][db][4 * j + 2], alpha, pr * lo_bf16(v.y));
+            O[qb][db][4 * j + 3] = fmaf(O[qb][db][4 * j + 3], alpha, pr * hi_bf16(v.y));
+          }
         }
       }
     }
@@ -204,22 +388,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_bf16_kernel(DecodeParams p)
     for (int qb = 0; qb < QB; ++qb) {
       mu[qb] = m[qb];
       lu[qb] = l[qb];
-      const float inv = 1.f / l[qb];
+      if (kh == 0) {
+        const float inv = 1.f / l[qb];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) Ou[qb][db] = O[qb][db] * inv;
-      const int64_t ri = qoff[qb] / D;
-      if (valid[qb]) {
-        if (p.stage_ml && hl == 0) {
-          p.stage_ml[(n_rows_all + ri) * 2 + 0] = m[qb] * p.scale;
-          p.stage_ml[(n_rows_all + ri) * 2 + 1] = l[qb];
-        }
-        if (p.stage_o) {
+        for (int db = 0; db < NDB; ++db) Ou[qb][db] = O[qb][db] * inv;
+        const int64_t ri = qoff[qb] / D;
+        if (valid[qb]) {
+          if (p.stage_ml && hl == 0) {
+            p.stage_ml[(n_rows_all + ri) * 2 + 0] = m[qb] * p.scale;
+            p.stage_ml[(n_rows_all + ri) * 2 + 1] = l[qb];
+          }
+          if (p.stage_o) {
 #pragma unroll
-          for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              p.stage_o[(n_rows_all + ri) * D + db * 32 + 8 * (e / 4) + 4 * hl + e % 4] =
-                  Ou[qb][db][e];
+              for (int e = 0; e < 16; ++e)
+                p.stage_o[(n_rows_all + ri) * D + db * 32 + 8 * (e / 4) + 4 * hl + e % 4] =
+                    Ou[qb][db][e];
+          }
         }
       }
       m[qb] = -INFINITY;
@@ -234,155 +420,137 @@ __global__ __launch_bounds__(WAVES * 64) void decode_bf16_kernel(DecodeParams p)
     for (int qb = 0; qb < QB; ++qb) l[qb] = hl == 0 ? l[qb] : 0.f;
   }
 
-  // ---- Shared stage
-  const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
-                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
-  const uint16_t *svg = static_cast<const uint16_t *>(p.shared_v) +
-                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
-  const int n_tiles = (L + KT - 1) / KT;
-  uint4 kreg[KPT];
-  uint4 vreg[VPT][4];
-
-  auto load_tile = [&](int key0) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + i * NT;
-      if (ch < KCH) {
-        const int key = key0 + ch / (D / 8);
-        kreg[i] = key < L ? *reinterpret_cast<const uint4 *>(skg + (int64_t)key * D +
-                                                              (ch % (D / 8)) * 8)
-                          : uint4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int bl = tid + i * NT;
-      if (bl < VBL) {
-        const int dc = bl % (D / 8);
-        const int key = key0 + 4 * (bl / (D / 8));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vreg[i][e] = key + e < L ? *reinterpret_cast<const uint4 *>(
-                                         svg + (int64_t)(key + e) * D + dc * 8)
-                                   : uint4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ch = tid + i * NT;
-      if (ch < KCH)
-        *reinterpret_cast<uint4 *>(&k_lds[buf][ch / (D / 8)][(ch % (D / 8)) * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int bl = tid + i * NT;
-      if (bl < VBL) {
-        const int dc = bl % (D / 8);
-        const int pos = vt_pos(4 * (bl / (D / 8)));
-        const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-        const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-        const uint32_t w2[4] = {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w};
-        const uint32_t w3[4] = {vreg[i][3].x, vreg[i][3].y, vreg[i][3].z, vreg[i][3].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // dims 2e and 2e+1 of the four keys
-          const uint2 even = {(w0[e] & 0xffffu) | (w1[e] << 16), (w2[e] & 0xffffu) | (w3[e] << 16)};
-          const uint2 odd = {(w0[e] >> 16) | (w1[e] & 0xffff0000u),
-                             (w2[e] >> 16) | (w3[e] & 0xffff0000u)};
-          *reinterpret_cast<uint2 *>(&vt_lds[buf][dc * 8 + 2 * e][pos]) = even;
-          *reinterpret_cast<uint2 *>(&vt_lds[buf][dc * 8 + 2 * e + 1][pos]) = odd;
-        }
-      }
-    }
-  };
-
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
+  // ---- Shared stage: tile `it` is in LDS buffer it & 1 and tile it + 1 is
+  // in flight in registers while tile it is consumed
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
     const int key0 = it * KT;
-    if (it + 1 < n_tiles) load_tile(key0 + KT);
+    const uint16_t *kl = T::k(lds, buf);
+    const uint16_t *vl = T::vt(lds, buf);
 
-    // S^T = K . Q^T for the two 32-key blocks of the tile
-    f32x16 sacc[2][QB];
+    // S^T = K . Q^T for this wave's 32-key block(s) of the tile
+    f32x16 sacc[NKB][QB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < NKB; ++i)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16{};
+      for (int qb = 0; qb < QB; ++qb) sacc[i][qb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&k_lds[buf][kb * 32 + ql][ks * 16 + hl * 8]);
+      for (int i = 0; i < NKB; ++i) {
+        const int kb = kh * NKB + i;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kl + (kb * 32 + ql) * T::kPitch +
+                                                           ks * 16 + hl * 8);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma(a, qf[qb][ks], sacc[kb][qb]);
+        for (int qb = 0; qb < QB; ++qb) sacc[i][qb] = mfma(a, qf[qb][ks], sacc[i][qb]);
       }
     }
 
     // online softmax (scores stay in raw dot units; exp2 with scale*log2e)
     const bool tail = key0 + KT > L;
-    bf16x8 pf[QB][4];
+    bf16x8 pf[QB][2 * NKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 0; i < NKB; ++i) {
+        const int kb = kh * NKB + i;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           if (tail) {
             const int key = key0 + kb * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-            if (key >= L) sacc[kb][qb][e] = -INFINITY;
+            if (key >= L) sacc[i][qb][e] = -INFINITY;
           }
-          tmax = fmaxf(tmax, sacc[kb][qb][e]);
+          tmax = fmaxf(tmax, sacc[i][qb][e]);
         }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(m[qb], tmax);
-      const float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c);
-      const float mc = mn * c;
+      tmax = pair_max(tmax);
+      if (__any(tmax > m[qb] + thr)) {
+        const float mn = fmaxf(m[qb], tmax);
+        const float alpha = __builtin_amdgcn_exp2f((m[qb] - mn) * c);
+        m[qb] = mn;
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) O[qb][db] *= alpha;
+      }
+      // a key half can see only masked keys: m stays -inf and p = 0
+      const float mc = m[qb] == -INFINITY ? 0.f : m[qb] * c;
       float lsum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 0; i < NKB; ++i) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][e], c, -mc));
-          sacc[kb][qb][e] = pe;
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[i][qb][e], c, -mc));
+          sacc[i][qb][e] = pe;
           lsum += pe;
         }
       }
-      l[qb] = fmaf(l[qb], alpha, lsum);
-      m[qb] = mn;
+      l[qb] += lsum;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) O[qb][db] *= alpha;
-#pragma unroll
-      for (int ps = 0; ps < 4; ++ps) pf[qb][ps] = to_bf16x8(sacc[ps >> 1][qb], 8 * (ps & 1));
+      for (int j = 0; j < 2 * NKB; ++j) pf[qb][j] = to_bf16x8(sacc[j >> 1][qb], 8 * (j & 1));
     }
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T over this wave's keys
 #pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
+    for (int j = 0; j < 2 * NKB; ++j) {
+      const int ps = 2 * kh * NKB + j;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&vt_lds[buf][db * 32 + ql][ps * 16 + hl * 8]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vl + (db * 32 + ql) * T::vPitch +
+                                                           ps * 16 + hl * 8);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) O[qb][db] = mfma(a, pf[qb][ps], O[qb][db]);
+        for (int qb = 0; qb < QB; ++qb) O[qb][db] = mfma(a, pf[qb][j], O[qb][db]);
       }
     }
 
-    if (it + 1 < n_tiles) store_tile(buf ^ 1);
+    if (it + 1 < n_tiles) tile_store<D, NT>(stage, tid, lds, buf ^ 1);
     __syncthreads();
+    if (it + 2 < n_tiles) tile_load<D, NT>(stage, tid, skg, svg, key0 + 2 * KT, L);
+  }
+
+  // ---- the second key half hands its state to the first through LDS
+  if constexpr (KSPLIT == 2) {
+    float *xo = reinterpret_cast<float *>(lds) + rg * (QB * (NDB * 16 + 2) * 64);
+    if (kh == 1) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float *dst = xo + qb * (NDB * 16 + 2) * 64;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) dst[(db * 16 + e) * 64 + lane] = O[qb][db][e];
+        dst[(NDB * 16) * 64 + lane] = m[qb];
+        dst[(NDB * 16 + 1) * 64 + lane] = l[qb];
+      }
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float *src = xo + qb * (NDB * 16 + 2) * 64;
+      const float m2 = src[(NDB * 16) * 64 + lane];
+      const float l2 = src[(NDB * 16 + 1) * 64 + lane];
+      float a1 = 1.f, a2 = 0.f;
+      if (m2 > m[qb]) {
+        a1 = __builtin_amdgcn_exp2f((m[qb] - m2) * c);  // 0 when m is -inf
+        a2 = 1.f;
+        m[qb] = m2;
+      } else if (m2 != -INFINITY) {
+        a2 = __builtin_amdgcn_exp2f((m2 - m[qb]) * c);
+      }
+      l[qb] = l[qb] * a1 + l2 * a2;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          O[qb][db][e] = O[qb][db][e] * a1 + src[(db * 16 + e) * 64 + lane] * a2;
+    }
   }
 
   // ---- Merge / epilogue
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const float lt = pair_sum(l[qb]);
     if constexpr (TAPS) {
       // Shared partial (m, lt, O / lt) on its own, then the explicit
       // OnlineSoftmax merge with the Unshared partial (mu, lu, Ou).
@@ -430,9 +598,9 @@ __global__ __launch_bounds__(WAVES * 64) void decode_bf16_kernel(DecodeParams p)
   }
 }
 
-template <int D, int WAVES, int QB, bool TAPS>
+template <int D, int RG, int QB, int KSPLIT, bool TAPS>
 hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream) {
-  constexpr int ROWS = WAVES * QB * 32;
+  constexpr int ROWS = RG * QB * 32;
   DecodeParams p = p0;
   p.n_rb = (p.M + ROWS - 1) / ROWS;
   const int64_t grid = (int64_t)p.R * p.Hkv * p.n_rb;
@@ -442,47 +610,31 @@ hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream) {
     const int nb = min(p.BW, (ROWS - 1) / p.G + 2);
     dyn = (size_t)nb * (p.step + 1) * sizeof(int32_t);
   }
-  hipLaunchKernelGGL((decode_bf16_kernel<D, WAVES, QB, TAPS>), dim3((unsigned)grid),
-                     dim3(WAVES * 64), dyn, stream, p);
+  hipLaunchKernelGGL((decode_bf16_kernel<D, RG, QB, KSPLIT, TAPS>), dim3((unsigned)grid),
+                     dim3(RG * KSPLIT * 64), dyn, stream, p);
   return hipGetLastError();
 }
 
-struct TileChoice {
-  int waves, qb;
-};
-
-TileChoice choose_tile(const DecodeParams &p) {
-  if (p.M <= 32) return {1, 1};
-  if (p.M <= 64) return {2, 1};
-  if (p.M <= 128) return {4, 1};
-  // Two 32-row blocks per wave halve the LDS traffic per MFMA; use them
-  // when there are still enough workgroups to cover the 256 CUs twice.
-  const int64_t blocks_qb2 = (int64_t)p.R * p.Hkv * ((p.M + 255) / 256);
-  return blocks_qb2 >= 512 ? TileChoice{4, 2} : TileChoice{4, 1};
-}
+// Rows per workgroup: 32 (1 wave) or 64 (2 waves) for few query rows per
+// (request, KV head); otherwise 128 rows in 4 row groups x 2 key halves.
+int rows_per_block(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : 128); }
 
 template <int D>
 hipError_t launch_d(const DecodeParams &p, bool taps, hipStream_t stream) {
-  const TileChoice t = choose_tile(p);
+  const int rows = rows_per_block(p.M);
   if (taps) {
-    // the debug variant keeps a second stage state in registers: one
-    // 32-row block per wave
-    if (t.waves == 1) return launch_cfg<D, 1, 1, true>(p, stream);
-    if (t.waves == 2) return launch_cfg<D, 2, 1, true>(p, stream);
-    return launch_cfg<D, 4, 1, true>(p, stream);
+    if (rows == 32) return launch_cfg<D, 1, 1, 1, true>(p, stream);
+    if (rows == 64) return launch_cfg<D, 2, 1, 1, true>(p, stream);
+    return launch_cfg<D, 4, 1, 2, true>(p, stream);
   }
-  if (t.waves == 1) return launch_cfg<D, 1, 1, false>(p, stream);
-  if (t.waves == 2) return launch_cfg<D, 2, 1, false>(p, stream);
-  if (t.qb == 1) return launch_cfg<D, 4, 1, false>(p, stream);
-  return launch_cfg<D, 4, 2, false>(p, stream);
+  if (rows == 32) return launch_cfg<D, 1, 1, 1, false>(p, stream);
+  if (rows == 64) return launch_cfg<D, 2, 1, 1, false>(p, stream);
+  return launch_cfg<D, 4, 1, 2, false>(p, stream);
 }
 
 }  // namespace
 
-int bf16_rows_per_block(const DecodeParams &p) {
-  const TileChoice t = choose_tile(p);  // xattn_decode's tiling
-  return t.waves * t.qb * 32;
-}
+int bf16_rows_per_block(const DecodeParams &p) { return rows_per_block(p.M); }
 
 hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream) {
   if (p.D == 64) return launch_d<64>(p, taps, stream);
