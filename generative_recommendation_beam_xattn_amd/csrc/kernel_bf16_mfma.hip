@@ -46,6 +46,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -126,14 +127,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Geometry of one LDS stage: a K tile then a V tile, each KT rows of D
-// bf16, row-major, with the 16-byte slots of row r permuted by swz(r).
+// Geometry of the LDS tiles: per stage a K tile and a V tile (separate
+// LDS objects), each KT rows of D bf16, row-major, with the 16-byte slots
+// of row r permuted by swz(r).
 template <int D>
 struct TileGeom {
   static constexpr int RB = D * 2;                 // bytes per row
   static constexpr int SLOTS = D / 8;              // 16-byte slots per row
   static constexpr int TILE_BYTES = KT * RB;       // one K (or V) tile
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   static constexpr int ROWS_PER_COPY = 1024 / RB;  // rows one wave-wide 16-byte copy fills
   static constexpr int COPIES = 2 * TILE_BYTES / 1024;  // wave-wide copies per stage (K and V)
   // Slot permutation.  D = 128 (16 slots): swap the two 2-bit fields of
@@ -151,77 +152,147 @@ struct TileGeom {
   }
 };
 
-// Copy the K and V tile starting at key0 into `stage` (this wave's share of
-// the COPIES wave-wide copies).  Rows past the prompt are clamped to its
-// last row (always in bounds): their scores are masked and their
-// probabilities are exactly zero.
+// This wave's share of the COPIES wave-wide copies that fill one stage:
+// copy i moves 1 KiB = ROWS_PER_COPY rows of the K tile (first NQ copies)
+// or of the V tile.  Lane `lane` fetches row q * ROWS_PER_COPY + lane /
+// SLOTS, 16-byte chunk (lane % SLOTS) ^ swz(row), which lands in LDS slot
+// lane % SLOTS of that row.
 template <int D, int WAVES>
-__device__ __forceinline__ void tile_copy(uint8_t *stage, const uint16_t *skg, const uint16_t *svg,
-                                          int key0, int L, int wave, int lane) {
+struct CopyPlan {
   using Gm = TileGeom<D>;
-  constexpr int NQ = Gm::TILE_BYTES / 1024;   // copies per K (or V) tile
-  constexpr int PER = Gm::COPIES / WAVES;
+  static constexpr int NQ = Gm::TILE_BYTES / 1024;   // copies per K (or V) tile
+  static constexpr int PER = Gm::COPIES / WAVES;
   static_assert(Gm::COPIES % WAVES == 0, "copies must split evenly over the waves");
-  const int sub = lane / Gm::SLOTS;
-  const int slot = lane % Gm::SLOTS;
+  uint32_t off[PER];   // byte offset of this lane's 16-byte chunk from the tile's first row
+  __device__ void init(int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int qi = wave * PER + i;
-    const bool is_v = qi >= NQ;
-    const int q = is_v ? qi - NQ : qi;
-    const int row = q * Gm::ROWS_PER_COPY + sub;
-    const int key = min(key0 + row, L - 1);
-    const uint16_t *src = (is_v ? svg : skg) + (int64_t)key * D + (slot ^ Gm::swz(row)) * 8;
-    uint8_t *dst = stage + (is_v ? Gm::TILE_BYTES : 0) + q * 1024;
+    for (int i = 0; i < PER; ++i) {
+      const int qi = wave * PER + i;
+      const int q = qi >= NQ ? qi - NQ : qi;
+      const int row = q * Gm::ROWS_PER_COPY + lane / Gm::SLOTS;
+      off[i] = (uint32_t)(row * Gm::RB + (((lane % Gm::SLOTS) ^ Gm::swz(row)) << 4));
+    }
+  }
+  __device__ static int row_of(uint32_t off) { return (int)(off / Gm::RB); }
+};
+
+// Copy the KT key rows starting at key0 into one ring stage (ktile, vtile).
+// The caller keeps key0 + KT <= L whenever L >= KT (the last window is
+// shifted back to end at L), so only a prompt shorter than one tile needs
+// its rows clamped to the last one; clamped rows are always in bounds and
+// their scores are masked.
+template <int D, int WAVES, bool CLAMP>
+__device__ __forceinline__ void tile_copy(uint8_t *ktile, uint8_t *vtile,
+                                          const CopyPlan<D, WAVES> &cp, const uint16_t *skg,
+                                          const uint16_t *svg, int key0, int L, int wave) {
+  using Gm = TileGeom<D>;
+  using C = CopyPlan<D, WAVES>;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int qi = wave * C::PER + i;
+    const bool is_v = qi >= C::NQ;
+    const int q = is_v ? qi - C::NQ : qi;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(is_v ? svg : skg);
+    const uint8_t *src;
+    if constexpr (!CLAMP) {
+      src = base + (int64_t)key0 * Gm::RB + cp.off[i];
+    } else {
+      const int row = C::row_of(cp.off[i]);
+      const int key = min(key0 + row, L - 1);
+      src = base + (int64_t)key * Gm::RB + (cp.off[i] - (uint32_t)(row * Gm::RB));
+    }
+    uint8_t *dst = (is_v ? vtile : ktile) + q * 1024;
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
                                      (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
   }
 }
 
-// Per-lane state of one wave's 32 query rows.
+// Per-lane state of one wave's 32 query rows: running max m (raw dot-product
+// units), O^T accumulators for this lane's 64 dims, and l, the sum of
+// exp2((score - m) * c) over the keys this lane-pair has seen, split between
+// the two lanes of the pair (the row total is pair_sum(l)).
 template <int D>
 struct Rows {
   float m, l;
   f32x16 O[D / 32];
+  __device__ void clear() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) O[db] = f32x16{};
+  }
 };
 
-// One 64-key tile from `stage`: this wave's 32-key block(s) of S^T, the
-// online-softmax update and the PV contraction.
-template <int D, int KSPLIT>
-__device__ __forceinline__ void consume_tile(const uint8_t *stage, const bf16x8 (&qf)[D / 16],
-                                             Rows<D> &st, int kh, int key0, int L, float c,
-                                             float thr, int lane) {
+// Per-lane LDS byte offsets of the MFMA A-operand fragments within a tile.
+// K (ds_read_b128): row kh*NKB*32 + 32*i + ql, 16-byte slot (2ks + hl) ^
+// swz(ql) -- the block index i only adds a multiple of 32 rows, so it is an
+// immediate.  V^T (ds_read_b64_tr_b16): for k-step ps, half e2 and O block
+// db the row is 32*(ps/2) + 16*(ps%2) + 8*e2 + 4h + j/4 and the slot
+// (4db + 2g + (j/2)%2) ^ swz(row); swz(row) depends only on the lane and e2
+// (the ps terms are multiples of 16 rows), so ps is an immediate as well.
+template <int D>
+struct FragOffsets {
   using Gm = TileGeom<D>;
-  constexpr int NKS = D / 16, NDB = D / 32, NKB = 2 / KSPLIT;
-  const int hl = lane >> 5, ql = lane & 31;
+  uint32_t k[D / 16];        // per ks
+  uint32_t v[2][D / 32];     // per e2, db
+  __device__ void init(int kh, int nkb, int lane) {
+    const int hl = lane >> 5, ql = lane & 31;
+    const int kswz = Gm::swz(ql);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      k[ks] = (uint32_t)((kh * nkb * 32 + ql) * Gm::RB + (((2 * ks + hl) ^ kswz) << 4));
+    const int vh = lane >> 5, vg = (lane >> 4) & 1, vj = lane & 15;
+#pragma unroll
+    for (int e2 = 0; e2 < 2; ++e2) {
+      const int row = e2 * 8 + vh * 4 + (vj >> 2);   // plus multiples of 16
+      const int sw = Gm::swz(row);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int chunk = 4 * db + 2 * vg + ((vj >> 1) & 1);
+        v[e2][db] = (uint32_t)(row * Gm::RB + ((chunk ^ sw) << 4) + ((vj & 1) << 3));
+      }
+    }
+  }
+};
 
-  // S^T = K . Q^T
-  const int kswz = Gm::swz(ql);  // rows kb * 32 + ql share the permutation of row ql
-  f32x16 sacc[NKB];
+// S^T = K . Q^T for this wave's 32-key block(s) of the tile in `ktile`.
+template <int D, int KSPLIT>
+__device__ __forceinline__ void qk_tile(const uint8_t *ktile, const bf16x8 (&qf)[D / 16],
+                                        f32x16 (&sacc)[2 / KSPLIT], const FragOffsets<D> &fo) {
+  using Gm = TileGeom<D>;
+  constexpr int NKS = D / 16, NKB = 2 / KSPLIT;
 #pragma unroll
   for (int i = 0; i < NKB; ++i) sacc[i] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
     for (int i = 0; i < NKB; ++i) {
-      const int kb = kh * NKB + i;
-      const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-          stage + (kb * 32 + ql) * Gm::RB + (((2 * ks + hl) ^ kswz) << 4));
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8 *>(ktile + fo.k[ks] + i * 32 * Gm::RB);
       sacc[i] = mfma(a, qf[ks], sacc[i]);
     }
   }
+}
 
-  // online softmax (scores stay in raw dot units; exp2 with scale*log2e)
+// Online-softmax update with one tile's scores, part 1: with TAIL, mask
+// the keys outside [lo, L) (the tile holds keys key0 ..); take the row
+// maximum and raise m lazily (rescaling l and O when it moves).  Returns
+// m * c, the exp2 offset of part 2.
+template <int D, int KSPLIT, bool TAIL>
+__device__ __forceinline__ float softmax_max(f32x16 (&sacc)[2 / KSPLIT], Rows<D> &st, int kh,
+                                             int key0, int lo, int L, float c, float thr,
+                                             int lane) {
+  constexpr int NDB = D / 32, NKB = 2 / KSPLIT;
+  const int hl = lane >> 5;
   float tmax = -INFINITY;
-  const bool tail = key0 + KT > L;
 #pragma unroll
   for (int i = 0; i < NKB; ++i) {
     const int kb = kh * NKB + i;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if (tail) {
+      if constexpr (TAIL) {
         const int key = key0 + kb * 32 + 8 * (e / 4) + 4 * hl + (e % 4);
-        if (key >= L) sacc[i][e] = -INFINITY;
+        if (key < lo || key >= L) sacc[i][e] = -INFINITY;
       }
       tmax = fmaxf(tmax, sacc[i][e]);
     }
@@ -236,47 +307,174 @@ __device__ __forceinline__ void consume_tile(const uint8_t *stage, const bf16x8 
     for (int db = 0; db < NDB; ++db) st.O[db] *= alpha;
   }
   // a key half can see only masked keys: m stays -inf and p = 0
-  const float mc = st.m == -INFINITY ? 0.f : st.m * c;
-  float lsum = 0.f;
-  bf16x8 pf[2 * NKB];
+  return st.m == -INFINITY ? 0.f : st.m * c;
+}
+
+// Part 2 (branch-free): probabilities exp2(s * c - mc) as bf16 (the B
+// operand of the PV product) and their sum into l, two per
+// v_dot2_f32_bf16 against (1, 1), so l sums exactly the values PV uses.
+template <int D, int KSPLIT>
+__device__ __forceinline__ void softmax_exp(f32x16 (&sacc)[2 / KSPLIT], bf16x8 (&pf)[4 / KSPLIT],
+                                            Rows<D> &st, float c, float mc) {
+  constexpr int NKB = 2 / KSPLIT;
 #pragma unroll
   for (int i = 0; i < NKB; ++i) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[i][e], c, -mc));
-      sacc[i][e] = pe;
-      lsum += pe;
-    }
+    for (int e = 0; e < 16; ++e) sacc[i][e] = __builtin_amdgcn_exp2f(fmaf(sacc[i][e], c, -mc));
     pf[2 * i] = to_bf16x8(sacc[i], 0);
     pf[2 * i + 1] = to_bf16x8(sacc[i], 8);
   }
-  st.l += lsum;
-
-  // O^T += V^T . P^T.  For k-step ps (16 keys) the B operand of lane half
-  // h holds the keys 32*(ps/2) + 16*(ps%2) + 8*e2 + 4h + (0..3), e2 = 0, 1;
-  // each half-fragment of V^T is one transposing read: lane j of a 16-lane
-  // group points at 4 dims of key row base + j/4, and receives 4 keys of
-  // dim d0 + (lane % 16).
-  const uint8_t *vt = stage + Gm::TILE_BYTES;
-  const int vh = lane >> 5, vg = (lane >> 4) & 1, vj = lane & 15;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int j2 = 0; j2 < 2 * NKB; ++j2) {
-    const int ps = 2 * kh * NKB + j2;
+  for (int j = 0; j < 2 * NKB; ++j) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      bf16x4 half_frag[2];
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const int row = (ps >> 1) * 32 + (ps & 1) * 16 + e2 * 8 + vh * 4 + (vj >> 2);
-        const int chunk = 4 * db + 2 * vg + ((vj >> 1) & 1);
-        const uint8_t *addr = vt + row * Gm::RB + ((chunk ^ Gm::swz(row)) << 4) + ((vj & 1) << 3);
-        half_frag[e2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)addr);
-      }
-      const bf16x8 a = {half_frag[0][0], half_frag[0][1], half_frag[0][2], half_frag[0][3],
-                        half_frag[1][0], half_frag[1][1], half_frag[1][2], half_frag[1][3]};
-      st.O[db] = mfma(a, pf[j2], st.O[db]);
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pr = {pf[j][e], pf[j][e + 1]};
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l, false);
     }
   }
+}
+
+// The S^T MFMAs of the next tile interleaved, k-step by k-step, with part 2
+// of the current tile's softmax: each k-step prefetches the next K
+// fragment, issues its MFMA(s) and then a share of the exponentials, their
+// bf16 packing and row sum, so the VALU works while the matrix core runs.
+// sched_barrier fences keep that order through scheduling.
+template <int D, int KSPLIT>
+__device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf16x8 (&qf)[D / 16],
+                                                 f32x16 (&s_next)[2 / KSPLIT],
+                                                 f32x16 (&s_cur)[2 / KSPLIT],
+                                                 bf16x8 (&pf)[4 / KSPLIT], Rows<D> &st, float c,
+                                                 float mc, const FragOffsets<D> &fo) {
+  using Gm = TileGeom<D>;
+  constexpr int NKS = D / 16, NKB = 2 / KSPLIT;
+  constexpr int NV = 16 * NKB;        // scores per lane
+  constexpr int PER = NV / NKS;       // exponentials per k-step (even)
+  static_assert(PER % 2 == 0, "scores are packed in pairs");
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < NKB; ++i) s_next[i] = f32x16{};
+  bf16x8 a_cur[NKB];
+#pragma unroll
+  for (int i = 0; i < NKB; ++i)
+    a_cur[i] = *reinterpret_cast<const bf16x8 *>(ktile + fo.k[0] + i * 32 * Gm::RB);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    bf16x8 a_nxt[NKB];
+    if (ks + 1 < NKS) {
+#pragma unroll
+      for (int i = 0; i < NKB; ++i)
+        a_nxt[i] = *reinterpret_cast<const bf16x8 *>(ktile + fo.k[ks + 1] + i * 32 * Gm::RB);
+    }
+#pragma unroll
+    for (int i = 0; i < NKB; ++i) s_next[i] = mfma(a_cur[i], qf[ks], s_next[i]);
+#pragma unroll
+    for (int u = 0; u < PER; u += 2) {
+      const int v = ks * PER + u;      // score index: block v / 16, element v % 16
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][v & 15], c, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s_cur[v >> 4][(v + 1) & 15], c, -mc));
+      const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+      pf[v >> 3][v & 7] = pk[0];
+      pf[v >> 3][(v + 1) & 7] = pk[1];
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, st.l, false);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks + 1 < NKS) {
+#pragma unroll
+      for (int i = 0; i < NKB; ++i) a_cur[i] = a_nxt[i];
+    }
+  }
+}
+
+// O^T += V^T . P^T over this wave's keys of the tile in `vt`.  For k-step
+// ps (16 keys) the B operand of lane half h holds the keys 32*(ps/2) +
+// 16*(ps%2) + 8*e2 + 4h + (0..3), e2 = 0, 1; each half-fragment of V^T is one
+// transposing read: lane j of a 16-lane group points at 4 dims of key row
+// base + j/4, and receives 4 keys of dim d0 + (lane % 16).
+template <int D, int KSPLIT>
+__device__ __forceinline__ void pv_tile(const uint8_t *vt, const bf16x8 (&pf)[4 / KSPLIT],
+                                        Rows<D> &st, int kh, const FragOffsets<D> &fo) {
+  using Gm = TileGeom<D>;
+  constexpr int NDB = D / 32, NKB = 2 / KSPLIT;
+  const uint8_t *vbase = vt + kh * NKB * 32 * Gm::RB;
+  constexpr int NSTEP = 2 * NKB * NDB;
+  // fragment n: k-step j2 = n / NDB (rows 32*(j2/2) + 16*(j2%2)), block db = n % NDB
+  auto frag = [&](int n) {
+    const int j2 = n / NDB, db = n % NDB;
+    const int prow = (j2 >> 1) * 32 + (j2 & 1) * 16;
+    const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(vbase + fo.v[0][db] + prow * Gm::RB));
+    const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(vbase + fo.v[1][db] + prow * Gm::RB));
+    return bf16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  };
+  bf16x8 a_cur = frag(0);
+#pragma unroll
+  for (int n = 0; n < NSTEP; ++n) {
+    bf16x8 a_nxt;
+    if (n + 1 < NSTEP) a_nxt = frag(n + 1);
+    st.O[n % NDB] = mfma(a_cur, pf[n / NDB], st.O[n % NDB]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (n + 1 < NSTEP) a_cur = a_nxt;
+  }
+}
+
+// Unshared stage for levels t_first, t_first + t_stride, ... <= step:
+// the beam's own generated token at each level (its ancestor slot), folded
+// into `st` by the same online-softmax update.  Each lane holds half of the
+// query and half of the output dims, so a score is a pair sum and its
+// weight is counted in l by lane half 0 only.
+template <int D>
+__device__ __forceinline__ void unshared_tokens(Rows<D> &st, const bf16x8 (&qf)[D / 16],
+                                                const uint16_t *ukg, const uint16_t *uvg,
+                                                const int32_t *anc_row, const int32_t *anc_ws,
+                                                int64_t anc_ws_base, int BW, int step,
+                                                int t_first, int t_stride, float c, int lane) {
+  constexpr int NKS = D / 16, NDB = D / 32;
+  const int hl = lane >> 5;
+  for (int t = t_first; t <= step; t += t_stride) {
+    const int slot = anc_ws ? clampi(anc_ws[anc_ws_base + (int64_t)t * BW], 0, BW - 1) : anc_row[t];
+    const int64_t roff = ((int64_t)t * BW + slot) * D;
+    uint4 kr[NKS];
+    uint2 vr[NDB][4];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kr[ks] = *reinterpret_cast<const uint4 *>(ukg + roff + ks * 16 + hl * 8);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vr[db][j] = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) part = dot8(__builtin_bit_cast(uint4, qf[ks]), kr[ks], part);
+    const float sc = pair_sum(part);
+    const float mn = fmaxf(st.m, sc);
+    const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // 0 while m is -inf
+    const float pr = __builtin_amdgcn_exp2f((sc - mn) * c);
+    st.l = st.l * alpha + (hl == 0 ? pr : 0.f);
+    st.m = mn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 v = vr[db][j];
+        st.O[db][4 * j + 0] = fmaf(st.O[db][4 * j + 0], alpha, pr * lo_bf16(v.x));
+        st.O[db][4 * j + 1] = fmaf(st.O[db][4 * j + 1], alpha, pr * hi_bf16(v.x));
+        st.O[db][4 * j + 2] = fmaf(st.O[db][4 * j + 2], alpha, pr * lo_bf16(v.y));
+        st.O[db][4 * j + 3] = fmaf(st.O[db][4 * j + 3], alpha, pr * hi_bf16(v.y));
+      }
+    }
+  }
+}
+
+// Parent rows of levels 1..step are staged in LDS for the ancestor walk
+// when they fit this many ints; longer chains are resolved beforehand into
+// the workspace.
+constexpr int kParentLdsInts = 2048;
+
+__host__ __device__ inline bool stage_parents_in_lds(int step, int BW) {
+  return step > 0 && (int64_t)step * BW <= kParentLdsInts;
 }
 
 template <int D, int RG, int KSPLIT, bool TAPS>
@@ -286,20 +484,24 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   constexpr int ROWS = RG * 32;
   constexpr int NKS = D / 16;           // k-steps of the QK contraction
   constexpr int NDB = D / 32;           // 32-row blocks of O^T
+  constexpr int NKB = 2 / KSPLIT;       // 32-key blocks per wave per tile
   using Gm = TileGeom<D>;
-  constexpr int COPIES_PER_WAVE = Gm::COPIES / WAVES;
+  constexpr int CPW = Gm::COPIES / WAVES;   // wave-wide copies per wave per tile
+  constexpr int PPT = (kParentLdsInts + NT - 1) / NT;  // staged parent ints per thread
 
-  // one LDS object per ring stage, so the compiler tracks the copies into
-  // each stage separately
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[Gm::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[Gm::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage2[Gm::STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage3[Gm::STAGE_BYTES];
-  extern __shared__ int32_t anc_lds[];  // [beams of the block][step + 1]
+  // The tile ring: K tiles of stages 0..3, then V tiles of stages 0..3, in
+  // one LDS object at constant offsets.  Constant offsets let every
+  // fragment address be a per-lane register plus an immediate, and let the
+  // compiler see that a copy into one stage does not alias reads of
+  // another (so it adds no wait of its own in front of those reads).
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * NSTAGE * Gm::TILE_BYTES];
+  // dynamic: ancestor slots [beams of the block][step + 1], then (when
+  // staged) the parent rows [step][BW] of levels 1..step
+  extern __shared__ int32_t dyn_lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
   const int rg = wave % RG;     // row group
   const int kh = wave / RG;     // key half
   const int hl = lane >> 5;     // lane half
@@ -311,7 +513,6 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   const int r = unit / p.Hkv;
   const int k = unit % p.Hkv;
   const int G = p.G, BW = p.BW, step = p.step;
-  const int L = clampi(p.prompt_len[r], 0, p.Lmax);
   const float c = p.scale_log2;
   // in raw dot-product units; the debug variant reports the stages' true
   // maxima, so it raises m on every increase
@@ -320,18 +521,22 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   const int row0 = rb * ROWS;
   const int b_lo = row0 / G;
   const int nb = min(BW - b_lo, (ROWS - 1) / G + 2);
-  const int n_tiles = (L + KT - 1) / KT;
+  int32_t *anc_lds = dyn_lds;
+  int32_t *par_lds = dyn_lds + nb * (step + 1);
+  const bool walk_here = p.anc == nullptr;
+  const bool staged = walk_here && stage_parents_in_lds(step, BW);
 
-  // ---- start the tile pipeline: tiles 0 .. NSTAGE-2 in flight
-  const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
-                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
-  const uint16_t *svg = static_cast<const uint16_t *>(p.shared_v) +
-                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
-  if (n_tiles > 0) tile_copy<D, WAVES>(stage0, skg, svg, 0, L, wave, lane);
-  if (n_tiles > 1) tile_copy<D, WAVES>(stage1, skg, svg, KT, L, wave, lane);
-  if (n_tiles > 2) tile_copy<D, WAVES>(stage2, skg, svg, 2 * KT, L, wave, lane);
-
-  // ---- this wave's query rows
+  // ---- loads that depend on nothing, oldest first (vmcnt counts in
+  // order): parent rows for the walk, this wave's q rows
+  int32_t pv[PPT];
+  const int32_t *par = p.parent_idx + (int64_t)r * p.S * BW;
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int e = tid + i * NT;
+      pv[i] = e < step * BW ? par[BW + e] : 0;   // levels 1..step
+    }
+  }
   const uint16_t *qg = static_cast<const uint16_t *>(p.q);
   uint16_t *og = static_cast<uint16_t *>(p.out);
   const int row = row0 + rg * 32 + ql;
@@ -345,161 +550,155 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     qf[ks] = __builtin_bit_cast(bf16x8,
                                 *reinterpret_cast<const uint4 *>(qg + qoff + ks * 16 + hl * 8));
 
+  // ---- start the tile pipeline: tiles 0 .. NSTAGE-2 in flight
+  const int L = clampi(p.prompt_len[r], 0, p.Lmax);
+  const int n_tiles = (L + KT - 1) / KT;
+  const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  const uint16_t *svg = static_cast<const uint16_t *>(p.shared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  CopyPlan<D, WAVES> cplan;
+  cplan.init(wave, lane);
+  // Tile t covers keys [t*KT, t*KT + KT); the last one's window is shifted
+  // back to [L - KT, L) (when L >= KT) so that no copy needs clamping; its
+  // keys below (n_tiles - 1) * KT were already counted and get masked.
+  const int last_key0 = L >= KT ? L - KT : 0;
+#define XATTN_KT(S) (tiles + (S) * Gm::TILE_BYTES)
+#define XATTN_VT(S) (tiles + (NSTAGE + (S)) * Gm::TILE_BYTES)
+#define XATTN_KEY0(T) ((T) + 1 < n_tiles ? (T) * KT : last_key0)
+  if (L < KT) {
+    if (n_tiles > 0)
+      tile_copy<D, WAVES, true>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, 0, L, wave);
+  } else {
+    tile_copy<D, WAVES, false>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, XATTN_KEY0(0), L, wave);
+    if (n_tiles > 1)
+      tile_copy<D, WAVES, false>(XATTN_KT(1), XATTN_VT(1), cplan, skg, svg, XATTN_KEY0(1), L,
+                                 wave);
+    if (n_tiles > 2)
+      tile_copy<D, WAVES, false>(XATTN_KT(2), XATTN_VT(2), cplan, skg, svg, XATTN_KEY0(2), L,
+                                 wave);
+  }
+
   // ---- ancestor slots of the block's beams (short chains: walked here)
-  if (p.anc == nullptr) {
-    const int32_t *par = p.parent_idx + (int64_t)r * p.S * BW;
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int e = tid + i * NT;
+      if (e < step * BW) par_lds[e] = pv[i];
+    }
+    wait_vm_lgkm0<63>();  // lgkmcnt only
+    lds_barrier();
+  }
+  if (walk_here) {
     for (int i = tid; i < nb; i += NT) {
       int a = b_lo + i;
       int32_t *dst = anc_lds + i * (step + 1);
       dst[step] = a;
       for (int t = step; t >= 1; --t) {
-        a = clampi(par[(int64_t)t * BW + a], 0, BW - 1);
+        a = clampi(staged ? par_lds[(t - 1) * BW + a] : par[(int64_t)t * BW + a], 0, BW - 1);
         dst[t - 1] = a;
       }
     }
   }
-  __syncthreads();  // ancestor slots visible
 
-  // ---- Unshared stage: the beam's token at every level.  The debug variant
-  // keeps it in key half 0; otherwise the key halves take alternate levels
-  // (their partial states are merged with the rest at the end).
+  // ---- Shared stage.  Per tile t (in stage t % NSTAGE) but the last: wait
+  // for tile t + 1 and synchronise, start the copy of tile t + 3 into the
+  // stage tile t - 1 used, finish the row maxima of tile t, then issue the
+  // S^T MFMAs of tile t + 1 interleaved with the exponentials of tile t (the
+  // matrix cores and the VALU work side by side), then tile t's PV MFMAs.
+  FragOffsets<D> fo;
+  fo.init(kh, NKB, lane);
   Rows<D> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) st.O[db] = f32x16{};
-  if (!TAPS || kh == 0) {
-    const int t_first = TAPS ? 0 : kh;
-    const int t_stride = TAPS ? 1 : KSPLIT;
-    const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
-                          ((int64_t)r * p.Hkv + k) * p.S * BW * D;
-    const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
-                          ((int64_t)r * p.Hkv + k) * p.S * BW * D;
-    const int bi = beam - b_lo;
-    for (int t = t_first; t <= step; t += t_stride) {
-      const int slot = p.anc ? clampi(p.anc[((int64_t)r * (step + 1) + t) * BW + beam], 0, BW - 1)
-                             : anc_lds[bi * (step + 1) + t];
-      const int64_t roff = ((int64_t)t * BW + slot) * D;
-      uint4 kr[NKS];
-      uint2 vr[NDB][4];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        kr[ks] = *reinterpret_cast<const uint4 *>(ukg + roff + ks * 16 + hl * 8);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vr[db][j] = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
-      float part = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        part = dot8(__builtin_bit_cast(uint4, qf[ks]), kr[ks], part);
-      const float sc = pair_sum(part);
-      const float mn = fmaxf(st.m, sc);
-      const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // 0 while m is -inf
-      const float pr = __builtin_amdgcn_exp2f((sc - mn) * c);
-      st.l = st.l * alpha + pr;
-      st.m = mn;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint2 v = vr[db][j];
-          st.O[db][4 * j + 0] = fmaf(st.O[db][4 * j + 0], alpha, pr * lo_bf16(v.x));
-          st.O[db][4 * j + 1] = fmaf(st.O[db][4 * j + 1], alpha, pr * hi_bf16(v.x));
-          st.O[db][4 * j + 2] = fmaf(st.O[db][4 * j + 2], alpha, pr * lo_bf16(v.y));
-          st.O[db][4 * j + 3] = fmaf(st.O[db][4 * j + 3], alpha, pr * hi_bf16(v.y));
-        }
-      }
-    }
-  }
-
-  const int64_t n_rows_all = (int64_t)p.R * BW * p.Hq;
-  const int64_t ri = qoff / D;
-  // Debug variant: the Unshared partial is kept on its own (mu, lu, Ou),
-  // written as stage 1, and the running state restarts for the Shared stage.
-  float mu = -INFINITY, lu = 0.f;
-  f32x16 Ou[TAPS ? NDB : 1];
-  if constexpr (TAPS) {
-    mu = st.m;
-    lu = st.l;
-    if (kh == 0) {
-      const float inv = 1.f / st.l;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) Ou[db] = st.O[db] * inv;
-      if (valid) {
-        if (p.stage_ml && hl == 0) {
-          p.stage_ml[(n_rows_all + ri) * 2 + 0] = st.m * p.scale;
-          p.stage_ml[(n_rows_all + ri) * 2 + 1] = st.l;
-        }
-        if (p.stage_o) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              p.stage_o[(n_rows_all + ri) * D + db * 32 + 8 * (e / 4) + 4 * hl + e % 4] = Ou[db][e];
-        }
-      }
-    }
-    st.m = -INFINITY;
-    st.l = 0.f;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) st.O[db] = f32x16{};
+  st.clear();
+  f32x16 s_cur[NKB], s_next[NKB];
+  bf16x8 pf[2 * NKB];
+  if (n_tiles > 0) {
+    if (n_tiles > 2)
+      wait_vm_lgkm0<2 * CPW>();
+    else if (n_tiles > 1)
+      wait_vm_lgkm0<CPW>();
+    else
+      wait_vm_lgkm0<0>();
+    lds_barrier();  // tile 0 and the ancestor slots are visible
+    qk_tile<D, KSPLIT>(XATTN_KT(0), qf, s_cur, fo);
   } else {
-    // Seeded state: both lanes of a pair hold the full unshared sum; keep it
-    // in one lane so the final pair-sum counts it once.
-    st.l = hl == 0 ? st.l : 0.f;
+    wait_vm_lgkm0<63>();
+    lds_barrier();  // the ancestor slots are visible
   }
-
-  // ---- Shared stage.  Tile `it` sits in stage it % NSTAGE.  Before
-  // consuming it, every wave waits for its own copies of that tile (the
-  // copies of the NSTAGE-2 later tiles may stay in flight) and the
-  // workgroup synchronises; then the copy of tile it + NSTAGE - 1 goes into
-  // the stage consumed in the previous iteration.
-#define XATTN_STAGE(S) ((S) == 0 ? stage0 : ((S) == 1 ? stage1 : ((S) == 2 ? stage2 : stage3)))
-#define XATTN_TILE_STEP(ST)                                                        \
-  {                                                                                \
-    const int it = it0 + (ST);                                                     \
-    if (it >= n_tiles) break;                                                      \
-    if (it + NSTAGE - 2 < n_tiles)                                                 \
-      wait_vm_lgkm0<(NSTAGE - 2) * COPIES_PER_WAVE>();                             \
-    else                                                                           \
-      wait_vm_lgkm0<0>();                                                          \
-    lds_barrier();                                                                 \
-    if (it + NSTAGE - 1 < n_tiles)                                                 \
-      tile_copy<D, WAVES>(XATTN_STAGE(((ST) + NSTAGE - 1) % NSTAGE), skg, svg,     \
-                          (it + NSTAGE - 1) * KT, L, wave, lane);                  \
-    consume_tile<D, KSPLIT>(XATTN_STAGE(ST), qf, st, kh, it * KT, L, c, thr, lane); \
+#define XATTN_TILE_STEP(ST)                                                           \
+  {                                                                                   \
+    const int t = t0 + (ST);                                                          \
+    if (t + 1 >= n_tiles) break;                                                      \
+    if (t + 2 < n_tiles)                                                              \
+      wait_vm_lgkm0<CPW>();                                                           \
+    else                                                                              \
+      wait_vm_lgkm0<0>();                                                             \
+    lds_barrier();                                                                    \
+    if (t + 3 < n_tiles)                                                              \
+      tile_copy<D, WAVES, false>(XATTN_KT(((ST) + 3) % NSTAGE),                       \
+                                 XATTN_VT(((ST) + 3) % NSTAGE), cplan, skg, svg,      \
+                                 XATTN_KEY0(t + 3), L, wave);                         \
+    const float mc = softmax_max<D, KSPLIT, false>(s_cur, st, kh, 0, 0, L, c, thr, lane); \
+    qk_next_with_exp<D, KSPLIT>(XATTN_KT(((ST) + 1) % NSTAGE), qf, s_next, s_cur, pf, st, \
+                                c, mc, fo);                                           \
+    pv_tile<D, KSPLIT>(XATTN_VT(ST), pf, st, kh, fo);                                 \
+    _Pragma("unroll") for (int i = 0; i < NKB; ++i) s_cur[i] = s_next[i];             \
   }
   static_assert(NSTAGE == 4, "the tile loop below is unrolled for 4 stages");
-  for (int it0 = 0; it0 < n_tiles; it0 += NSTAGE) {
+  for (int t0 = 0; t0 + 1 < n_tiles; t0 += NSTAGE) {
     XATTN_TILE_STEP(0)
     XATTN_TILE_STEP(1)
     XATTN_TILE_STEP(2)
     XATTN_TILE_STEP(3)
   }
 #undef XATTN_TILE_STEP
+  if (n_tiles > 0) {  // the last tile: every copy has landed
+    const int t = n_tiles - 1;
+    const int lo = t * KT;            // keys below were counted by earlier tiles
+    const int key0 = XATTN_KEY0(t);   // first key the tile holds
+    const bool masked = key0 < lo || key0 + KT > L;
+    const float mc = masked
+        ? softmax_max<D, KSPLIT, true>(s_cur, st, kh, key0, lo, L, c, thr, lane)
+        : softmax_max<D, KSPLIT, false>(s_cur, st, kh, key0, lo, L, c, thr, lane);
+    softmax_exp<D, KSPLIT>(s_cur, pf, st, c, mc);
+    pv_tile<D, KSPLIT>(tiles + (NSTAGE + t % NSTAGE) * Gm::TILE_BYTES, pf, st, kh, fo);
+  }
+#undef XATTN_KEY0
+
+  // ---- Unshared stage (all copies have landed; its loads queue behind
+  // nothing).  Key halves take alternate levels; the debug variant keeps
+  // the stage on its own in key half 0, after the halves are merged.
+  const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  const int32_t *anc_row = anc_lds + (beam - b_lo) * (step + 1);
+  const int64_t anc_ws_base = (int64_t)r * (step + 1) * BW + beam;
+  if constexpr (!TAPS)
+    unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step, kh, KSPLIT, c,
+                       lane);
 
   // ---- the second key half hands its state to the first through LDS
   // (stage buffer rg holds row group rg's exchange)
   if constexpr (KSPLIT == 2) {
     static_assert(RG <= NSTAGE, "one stage buffer per row group");
-    static_assert((NDB * 16 + 2) * 64 * 4 <= Gm::STAGE_BYTES, "exchange must fit a stage");
+    static_assert(NDB * 16 * 64 * 4 <= Gm::TILE_BYTES, "the exchanged O must fit a K tile");
     wait_vm_lgkm0<0>();
     lds_barrier();  // every wave is done with the tile stages
-    float *xo = reinterpret_cast<float *>(XATTN_STAGE(rg));
+    float *xo = reinterpret_cast<float *>(XATTN_KT(rg));   // O
+    float *xs = reinterpret_cast<float *>(XATTN_VT(rg));   // m, l
     if (kh == 1) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) xo[(db * 16 + e) * 64 + lane] = st.O[db][e];
-      xo[(NDB * 16) * 64 + lane] = st.m;
-      xo[(NDB * 16 + 1) * 64 + lane] = st.l;
+      xs[lane] = st.m;
+      xs[64 + lane] = st.l;
     }
     __syncthreads();
     if (kh == 1) return;
-    const float m2 = xo[(NDB * 16) * 64 + lane];
-    const float l2 = xo[(NDB * 16 + 1) * 64 + lane];
+    const float m2 = xs[lane];
+    const float l2 = xs[64 + lane];
     float a1 = 1.f, a2 = 0.f;
     if (m2 > st.m) {
       a1 = __builtin_amdgcn_exp2f((st.m - m2) * c);  // 0 when m is -inf
@@ -515,36 +714,50 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       for (int e = 0; e < 16; ++e)
         st.O[db][e] = st.O[db][e] * a1 + xo[(db * 16 + e) * 64 + lane] * a2;
   }
-#undef XATTN_STAGE
+#undef XATTN_KT
+#undef XATTN_VT
 
   // ---- Merge / epilogue
-  const float lt = pair_sum(st.l);
+  const int64_t n_rows_all = (int64_t)p.R * BW * p.Hq;
+  const int64_t ri = qoff / D;
   if constexpr (TAPS) {
-    // Shared partial (m, lt, O / lt) on its own, then the explicit
-    // OnlineSoftmax merge with the Unshared partial (mu, lu, Ou).
-    const float ms = st.m;
-    const float inv_s = lt > 0.f ? 1.f / lt : 0.f;
+    // Shared partial (m, l, O) on its own; then the Unshared partial on its
+    // own; then their explicit OnlineSoftmax merge.
+    Rows<D> su;
+    su.clear();
+    unshared_tokens<D>(su, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step, 0, 1, c, lane);
+    const float ls = pair_sum(st.l), lu = pair_sum(su.l);
+    const float ms = st.m, mu = su.m;
+    const float inv_s = ls > 0.f ? 1.f / ls : 0.f;
+    const float inv_u = 1.f / lu;
     const float mm = fmaxf(ms, mu);
-    const float ws = lt > 0.f ? lt * __builtin_amdgcn_exp2f((ms - mm) * c) : 0.f;
+    const float ws = ls > 0.f ? ls * __builtin_amdgcn_exp2f((ms - mm) * c) : 0.f;
     const float wu = lu * __builtin_amdgcn_exp2f((mu - mm) * c);
     const float inv_z = 1.f / (ws + wu);
     if (valid) {
       if (p.stage_ml && hl == 0) {
-        p.stage_ml[ri * 2 + 0] = lt > 0.f ? ms * p.scale : -INFINITY;
-        p.stage_ml[ri * 2 + 1] = lt;
+        p.stage_ml[ri * 2 + 0] = ls > 0.f ? ms * p.scale : -INFINITY;
+        p.stage_ml[ri * 2 + 1] = ls;
+        p.stage_ml[(n_rows_all + ri) * 2 + 0] = mu * p.scale;
+        p.stage_ml[(n_rows_all + ri) * 2 + 1] = lu;
       }
       if (p.stage_o) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
-            p.stage_o[ri * D + db * 32 + 8 * (e / 4) + 4 * hl + e % 4] = st.O[db][e] * inv_s;
+          for (int e = 0; e < 16; ++e) {
+            const int d = db * 32 + 8 * (e / 4) + 4 * hl + e % 4;
+            p.stage_o[ri * D + d] = st.O[db][e] * inv_s;
+            p.stage_o[(n_rows_all + ri) * D + d] = su.O[db][e] * inv_u;
+          }
       }
       if (p.lse && hl == 0) p.lse[ri] = mm * p.scale + __logf(ws + wu);
     }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) st.O[db] = (st.O[db] * (inv_s * ws) + Ou[db] * wu) * inv_z;
+    for (int db = 0; db < NDB; ++db)
+      st.O[db] = (st.O[db] * (inv_s * ws) + su.O[db] * (inv_u * wu)) * inv_z;
   } else {
+    const float lt = pair_sum(st.l);
     const float inv = 1.f / lt;
     if (valid && p.lse && hl == 0) p.lse[ri] = st.m * p.scale + __logf(lt);
 #pragma unroll
@@ -574,6 +787,7 @@ hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream) {
   if (p.anc == nullptr) {
     const int nb = min(p.BW, (ROWS - 1) / p.G + 2);
     dyn = (size_t)nb * (p.step + 1) * sizeof(int32_t);
+    if (stage_parents_in_lds(p.step, p.BW)) dyn += (size_t)p.step * p.BW * sizeof(int32_t);
   }
   hipLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
                      dim3(RG * KSPLIT * 64), dyn, stream, p);
