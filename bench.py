@@ -15,7 +15,8 @@ Prints ONE JSON line.  `value` is beam-steps per second over the timed
 region (wall clock between two device synchronisations).  `roofline` covers
 the decode kernel: algorithmic bytes (unique KV rows + q + out + indices) or
 FLOPs per launch divided by the kernel's mean launch duration, measured with
-HIP events on the launch stream.  `cpu_baseline` times the float64 CPU
+a pair of HIP events bound to each kernel dispatch (xattn_decode_timed), so
+the duration is the kernel's own, as a kernel trace reports it.  `cpu_baseline` times the float64 CPU
 oracle on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -185,16 +186,15 @@ def main():
 
     def run_step(k, events=None):
         for i, call in enumerate(calls[k % n_rot]):
-            if events is not None:
-                events[2 * i].record(stream)
-            call(stream)
-            if events is not None:
-                events[2 * i + 1].record(stream)
+            call(stream, None if events is None else (events[2 * i], events[2 * i + 1]))
 
     for k in range(args.warmup):
         run_step(k)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
           for _ in range(args.steps)]
+    for row in ev:          # torch creates the HIP event at its first record
+        for e in row:
+            e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):

@@ -7,13 +7,13 @@ if it is missing: there is no fallback implementation.
 """
 from . import workloads  # noqa: F401  (seeded inputs; no attention arithmetic)
 
-__all__ = ["decode", "decode_debug", "resolve_ancestors", "workspace_size", "library_path",
-           "XattnError", "workloads"]
+_BINDING = ("decode", "decode_debug", "resolve_ancestors", "workspace_size", "library_path",
+            "XattnError", "PreparedDecode", "load")
+__all__ = list(_BINDING[:-1]) + ["workloads"]
 
 
 def __getattr__(name):
-    if name in ("decode", "decode_debug", "resolve_ancestors", "workspace_size",
-                "library_path", "XattnError", "load"):
+    if name in _BINDING:
         from . import binding
         return getattr(binding, name)
     raise AttributeError(name)

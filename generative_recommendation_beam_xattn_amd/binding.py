@@ -36,7 +36,7 @@ class Shape(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
-EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_workspace_size",
+EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_workspace_size",
            "xattn_resolve_ancestors", "xattn_status_string", "xattn_last_error")
 
 
@@ -60,6 +60,8 @@ def load():
         lib.xattn_decode.restype = ctypes.c_int
         lib.xattn_decode_debug.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
         lib.xattn_decode_debug.restype = ctypes.c_int
+        lib.xattn_decode_timed.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P, P, P]
+        lib.xattn_decode_timed.restype = ctypes.c_int
         lib.xattn_workspace_size.argtypes = [S, i32]
         lib.xattn_workspace_size.restype = sz
         lib.xattn_resolve_ancestors.argtypes = [S, P, i32, P, P]
@@ -92,6 +94,13 @@ def _ptr(t):
 def _stream(stream, device):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _event(ev):
+    h = ev.cuda_event
+    if not h:
+        raise ValueError("record the event once before binding it to a launch")
+    return ctypes.c_void_p(h)
 
 
 def _dtype_code(t) -> int:
@@ -228,8 +237,15 @@ class PreparedDecode:
                      _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v), _ptr(parent_idx),
                      int(step), _ptr(self.out), _ptr(self.ws), ws_bytes)
 
-    def __call__(self, stream=None):
-        st = self.lib.xattn_decode(*self.args, _stream(stream, self.device))
+    def __call__(self, stream=None, events=None):
+        """events: optional (start, stop) torch.cuda.Event pair, each already
+        recorded once (torch creates the HIP event on first record); they are
+        bound to the attention kernel's dispatch (xattn_decode_timed)."""
+        if events is None:
+            st = self.lib.xattn_decode(*self.args, _stream(stream, self.device))
+        else:
+            st = self.lib.xattn_decode_timed(*self.args, _stream(stream, self.device),
+                                             _event(events[0]), _event(events[1]))
         if st != XATTN_OK:
             _check(st)
         return self.out

@@ -63,7 +63,7 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
                  const int32_t *prompt_len, const void *unshared_k, const void *unshared_v,
                  const int32_t *parent_idx, int32_t step, void *out, float *lse,
                  float *stage_ml, float *stage_o, bool taps, void *workspace,
-                 size_t workspace_bytes, void *stream) {
+                 size_t workspace_bytes, void *stream, xattn::LaunchEvents ev = {}) {
   xattn_status st = check_shape(s, step);
   if (st != XATTN_OK) return st;
   if (!q || !prompt_len || !unshared_k || !unshared_v || !parent_idx || !out)
@@ -121,9 +121,9 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
     p.anc = anc;
   }
   if (s->dtype == XATTN_F32)
-    e = xattn::launch_decode_f32(p, hs);
+    e = xattn::launch_decode_f32(p, hs, ev);
   else
-    e = xattn::launch_decode_bf16(p, taps, hs);
+    e = xattn::launch_decode_bf16(p, taps, hs, ev);
   if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
   g_last_error[0] = '\0';
   return XATTN_OK;
@@ -150,6 +150,20 @@ xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const v
                                 size_t workspace_bytes, void *stream) {
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
              out, lse, stage_ml, stage_o, true, workspace, workspace_bytes, stream);
+}
+
+xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const void *shared_k,
+                                const void *shared_v, const int32_t *prompt_len,
+                                const void *unshared_k, const void *unshared_v,
+                                const int32_t *parent_idx, int32_t step, void *out,
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                void *start_event, void *stop_event) {
+  if (!start_event || !stop_event) return fail(XATTN_EINVAL, "both timing events are required");
+  xattn::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream, ev);
 }
 
 size_t xattn_workspace_size(const xattn_shape *shape, int32_t step) {

@@ -39,6 +39,8 @@
 // stream in, so the Merge is the first online-softmax update.  The debug
 // variant (TAPS) instead keeps the two stages apart, writes each stage's
 // (m, l, o) and merges them explicitly at the end.
+#include <hip/hip_ext.h>
+
 #include "xattn_internal.h"
 
 namespace xattn {
@@ -777,7 +779,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
 }
 
 template <int D, int RG, int KSPLIT, bool TAPS>
-hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream) {
+hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream, LaunchEvents ev) {
   constexpr int ROWS = RG * 32;
   DecodeParams p = p0;
   p.n_rb = (p.M + ROWS - 1) / ROWS;
@@ -789,8 +791,12 @@ hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream) {
     dyn = (size_t)nb * (p.step + 1) * sizeof(int32_t);
     if (stage_parents_in_lds(p.step, p.BW)) dyn += (size_t)p.step * p.BW * sizeof(int32_t);
   }
-  hipLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
-                     dim3(RG * KSPLIT * 64), dyn, stream, p);
+  if (ev.start)
+    hipExtLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
+                          dim3(RG * KSPLIT * 64), (uint32_t)dyn, stream, ev.start, ev.stop, 0u, p);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
+                       dim3(RG * KSPLIT * 64), dyn, stream, p);
   return hipGetLastError();
 }
 
@@ -800,25 +806,26 @@ hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream) {
 int rows_per_block(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : 128); }
 
 template <int D>
-hipError_t launch_d(const DecodeParams &p, bool taps, hipStream_t stream) {
+hipError_t launch_d(const DecodeParams &p, bool taps, hipStream_t stream, LaunchEvents ev) {
   const int rows = rows_per_block(p.M);
   if (taps) {
-    if (rows == 32) return launch_cfg<D, 1, 2, true>(p, stream);
-    if (rows == 64) return launch_cfg<D, 2, 2, true>(p, stream);
-    return launch_cfg<D, 4, 2, true>(p, stream);
+    if (rows == 32) return launch_cfg<D, 1, 2, true>(p, stream, ev);
+    if (rows == 64) return launch_cfg<D, 2, 2, true>(p, stream, ev);
+    return launch_cfg<D, 4, 2, true>(p, stream, ev);
   }
-  if (rows == 32) return launch_cfg<D, 1, 2, false>(p, stream);
-  if (rows == 64) return launch_cfg<D, 2, 2, false>(p, stream);
-  return launch_cfg<D, 4, 2, false>(p, stream);
+  if (rows == 32) return launch_cfg<D, 1, 2, false>(p, stream, ev);
+  if (rows == 64) return launch_cfg<D, 2, 2, false>(p, stream, ev);
+  return launch_cfg<D, 4, 2, false>(p, stream, ev);
 }
 
 }  // namespace
 
 int bf16_rows_per_block(const DecodeParams &p) { return rows_per_block(p.M); }
 
-hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream) {
-  if (p.D == 64) return launch_d<64>(p, taps, stream);
-  if (p.D == 128) return launch_d<128>(p, taps, stream);
+hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream,
+                              LaunchEvents ev) {
+  if (p.D == 64) return launch_d<64>(p, taps, stream, ev);
+  if (p.D == 128) return launch_d<128>(p, taps, stream, ev);
   return hipErrorInvalidValue;
 }
 

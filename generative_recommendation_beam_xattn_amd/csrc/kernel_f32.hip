@@ -11,6 +11,8 @@
 // wave-reduced, and each wave keeps an online-softmax state per stage.  The
 // four waves' states are merged per stage in LDS, then the Shared and
 // Unshared partials are merged with the OnlineSoftmax combine.
+#include <hip/hip_ext.h>
+
 #include "xattn_internal.h"
 
 namespace xattn {
@@ -165,13 +167,26 @@ __global__ __launch_bounds__(kWaves * 64) void decode_f32_kernel(DecodeParams p)
 
 }  // namespace
 
-hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream) {
+namespace {
+
+template <int D>
+void launch_f32_d(const DecodeParams &p, unsigned grid, hipStream_t stream, LaunchEvents ev) {
+  if (ev.start)
+    hipExtLaunchKernelGGL(decode_f32_kernel<D>, dim3(grid), dim3(kWaves * 64), 0u, stream,
+                          ev.start, ev.stop, 0u, p);
+  else
+    hipLaunchKernelGGL(decode_f32_kernel<D>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
+}
+
+}  // namespace
+
+hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev) {
   const int64_t grid = (int64_t)p.R * p.BW * p.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (p.D == 64)
-    hipLaunchKernelGGL(decode_f32_kernel<64>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+    launch_f32_d<64>(p, (unsigned)grid, stream, ev);
   else if (p.D == 128)
-    hipLaunchKernelGGL(decode_f32_kernel<128>, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+    launch_f32_d<128>(p, (unsigned)grid, stream, ev);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -39,11 +39,19 @@ struct AncLayout {
   int64_t stride_r, stride_b, stride_t;
 };
 
+// Optional pair of events bound to one kernel dispatch (hipExtLaunchKernel):
+// start and stop then time that kernel alone.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 hipError_t launch_resolve_ancestors(const int32_t *parent_idx, int32_t R, int32_t BW, int32_t S,
                                     int32_t step, int32_t *anc, AncLayout layout,
                                     hipStream_t stream);
-hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream);
-hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream,
+                              LaunchEvents ev = {});
+hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev = {});
 
 // Number of query rows one bf16 workgroup owns for this shape.
 int bf16_rows_per_block(const DecodeParams &p);

@@ -135,6 +135,22 @@ xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const v
                                 float *lse, float *stage_ml, float *stage_o, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/*
+ * xattn_decode for measurement: identical work and results, and in addition
+ * start_event / stop_event (hipEvent_t, created by the caller, both required)
+ * are bound to the dispatch of the attention kernel itself, so
+ * hipEventElapsedTime(start_event, stop_event) is that kernel's execution
+ * time, with no queue or marker latency around it.  When the chain is deep
+ * enough to need the ancestor kernel, that kernel runs before start_event.
+ * Returns XATTN_EINVAL if an event is NULL.
+ */
+xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const void *shared_k,
+                                const void *shared_v, const int32_t *prompt_len,
+                                const void *unshared_k, const void *unshared_v,
+                                const int32_t *parent_idx, int32_t step, void *out,
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                void *start_event, void *stop_event);
+
 /* Static description of a status code. */
 const char *xattn_status_string(xattn_status status);
 

@@ -106,6 +106,15 @@ def test_bad_step_and_null_pointers_rejected(lib):
     assert lib.xattn_decode(None, *([None] * 7), 0, None, None, 0, None) == 1
 
 
+def test_timed_entry_requires_both_events(lib):
+    s = shape()
+    fake = ctypes.c_void_p(0x1000)
+    for start, stop in ((None, fake), (fake, None), (None, None)):
+        st = lib.xattn_decode_timed(ctypes.byref(s), *([None] * 7), 0, None, None, 0, None,
+                                    start, stop)
+        assert st == 1 and "event" in lib.xattn_last_error().decode()
+
+
 needs_no_gpu = pytest.mark.skipif(
     os.environ.get("HIP_VISIBLE_DEVICES", "") != "-1" and
     __import__("torch").cuda.is_available(),

@@ -187,6 +187,32 @@ def test_bitwise_deterministic_and_out_buffer_reuse():
     assert torch.equal(a.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("case", ["bf16_gr_serving", "f32_small", "bf16_deep_chain"])
+def test_timed_entry_matches_decode(case):
+    if case == "bf16_gr_serving":
+        w, i = W.make(2, R=4), 2
+    elif case == "f32_small":
+        w, i = W.custom(name="t32", seed=7, R=2, BW=5, Hq=8, Hkv=2, D=64, L=[70, 130],
+                        steps=[1], S=2, dtype="f32"), 0
+    else:
+        w, i = W.custom(name="tdeep", seed=8, R=2, BW=6, Hq=4, Hkv=2, D=128, L=[50, 90],
+                        steps=[30], S=31), 0
+    dw = DeviceWorkload(w)
+    say("[timed %s] step %d" % (case, w.steps[i]))
+    ref = X.decode(*dw.args(i))
+    call = X.PreparedDecode(*dw.args(i)[:8])
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in evs:
+        e.record(stream)
+    out = call(stream, events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref,
+                       out.view(torch.int16) if out.dtype == torch.bfloat16 else out)
+    t = evs[0].elapsed_time(evs[1])
+    assert 0.0 < t < 1000.0
+
+
 def test_invalid_arguments_raise_before_launch():
     w = W.custom(name="inv", seed=1, R=1, BW=2, Hq=2, Hkv=1, D=128, L=[8], steps=[0], S=2)
     dw = DeviceWorkload(w)
