@@ -426,47 +426,79 @@ __device__ __forceinline__ void pv_tile(const uint8_t *vt, const bf16x8 (&pf)[4 
 // into `st` by the same online-softmax update.  Each lane holds half of the
 // query and half of the output dims, so a score is a pair sum and its
 // weight is counted in l by lane half 0 only.
+// One generated token's K and V row, as the lanes of a row hold them: lane
+// half hl takes elements [8 hl, 8 hl + 8) of every 16 of K and the four
+// element groups of V the O^T accumulator layout gives it.
+template <int D>
+struct TokenRows {
+  uint4 kr[D / 16];
+  uint2 vr[D / 32][4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_token(TokenRows<D> &tr, const uint16_t *ukg,
+                                           const uint16_t *uvg, int64_t roff, int hl) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    tr.kr[ks] = *reinterpret_cast<const uint4 *>(ukg + roff + ks * 16 + hl * 8);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      tr.vr[db][j] = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
+}
+
+// Online-softmax update of a row's state with one token (fp32 dot product
+// on the VALU; the pair of lanes holding the row adds its two halves).
+template <int D>
+__device__ __forceinline__ void add_token(Rows<D> &st, const bf16x8 (&qf)[D / 16],
+                                          const TokenRows<D> &tr, float c, int hl) {
+  float part = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    part = dot8(__builtin_bit_cast(uint4, qf[ks]), tr.kr[ks], part);
+  const float sc = pair_sum(part);
+  const float mn = fmaxf(st.m, sc);
+  const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // 0 while m is -inf
+  const float pr = __builtin_amdgcn_exp2f((sc - mn) * c);
+  st.l = st.l * alpha + (hl == 0 ? pr : 0.f);
+  st.m = mn;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 v = tr.vr[db][j];
+      st.O[db][4 * j + 0] = fmaf(st.O[db][4 * j + 0], alpha, pr * lo_bf16(v.x));
+      st.O[db][4 * j + 1] = fmaf(st.O[db][4 * j + 1], alpha, pr * hi_bf16(v.x));
+      st.O[db][4 * j + 2] = fmaf(st.O[db][4 * j + 2], alpha, pr * lo_bf16(v.y));
+      st.O[db][4 * j + 3] = fmaf(st.O[db][4 * j + 3], alpha, pr * hi_bf16(v.y));
+    }
+  }
+}
+
+// Unshared stage for the row this lane pair holds: the tokens at levels
+// t_first, t_first - t_stride, ... >= 0, each the row of the beam's
+// ancestor slot at that level.  Levels are walked downwards so that the
+// first one can be the current level, whose slot is the beam itself: its
+// rows may have been loaded before the ancestor walk (`pre`, when has_pre).
 template <int D>
 __device__ __forceinline__ void unshared_tokens(Rows<D> &st, const bf16x8 (&qf)[D / 16],
                                                 const uint16_t *ukg, const uint16_t *uvg,
                                                 const int32_t *anc_row, const int32_t *anc_ws,
-                                                int64_t anc_ws_base, int BW, int step,
-                                                int t_first, int t_stride, float c, int lane) {
-  constexpr int NKS = D / 16, NDB = D / 32;
+                                                int64_t anc_ws_base, int BW, int t_first,
+                                                int t_stride, float c, int lane,
+                                                const TokenRows<D> &pre, bool has_pre) {
   const int hl = lane >> 5;
-  for (int t = t_first; t <= step; t += t_stride) {
-    const int slot = anc_ws ? clampi(anc_ws[anc_ws_base + (int64_t)t * BW], 0, BW - 1) : anc_row[t];
-    const int64_t roff = ((int64_t)t * BW + slot) * D;
-    uint4 kr[NKS];
-    uint2 vr[NDB][4];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      kr[ks] = *reinterpret_cast<const uint4 *>(ukg + roff + ks * 16 + hl * 8);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vr[db][j] = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
-    float part = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) part = dot8(__builtin_bit_cast(uint4, qf[ks]), kr[ks], part);
-    const float sc = pair_sum(part);
-    const float mn = fmaxf(st.m, sc);
-    const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // 0 while m is -inf
-    const float pr = __builtin_amdgcn_exp2f((sc - mn) * c);
-    st.l = st.l * alpha + (hl == 0 ? pr : 0.f);
-    st.m = mn;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint2 v = vr[db][j];
-        st.O[db][4 * j + 0] = fmaf(st.O[db][4 * j + 0], alpha, pr * lo_bf16(v.x));
-        st.O[db][4 * j + 1] = fmaf(st.O[db][4 * j + 1], alpha, pr * hi_bf16(v.x));
-        st.O[db][4 * j + 2] = fmaf(st.O[db][4 * j + 2], alpha, pr * lo_bf16(v.y));
-        st.O[db][4 * j + 3] = fmaf(st.O[db][4 * j + 3], alpha, pr * hi_bf16(v.y));
-      }
-    }
+  if (has_pre && t_first >= 0) {
+    add_token<D>(st, qf, pre, c, hl);
+    t_first -= t_stride;
+  }
+  TokenRows<D> tr;
+  for (int t = t_first; t >= 0; t -= t_stride) {
+    const int slot =
+        anc_ws ? clampi(anc_ws[anc_ws_base + (int64_t)t * BW], 0, BW - 1) : anc_row[t];
+    load_token<D>(tr, ukg, uvg, ((int64_t)t * BW + slot) * D, hl);
+    add_token<D>(st, qf, tr, c, hl);
   }
 }
 
@@ -552,15 +584,36 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     qf[ks] = __builtin_bit_cast(bf16x8,
                                 *reinterpret_cast<const uint4 *>(qg + qoff + ks * 16 + hl * 8));
 
-  // ---- start the tile pipeline: tiles 0 .. NSTAGE-2 in flight
-  const int L = clampi(p.prompt_len[r], 0, p.Lmax);
-  const int n_tiles = (L + KT - 1) / KT;
+  // ---- the current level's token rows (its slot is the beam itself, so no
+  // ancestor is needed): key half 0 starts them now
+  const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  TokenRows<D> cur_tok;
+  const bool early_tok = !TAPS && kh == 0;
+  if (early_tok) load_token<D>(cur_tok, ukg, uvg, ((int64_t)step * BW + beam) * D, hl);
+
+  // ---- start the tile pipeline: tiles 0 .. NSTAGE-2 in flight.  When the
+  // cache holds at least three tiles of rows, the copies of keys [0, 3 KT)
+  // start at once, before the prompt length is known (rows at or past it
+  // are allocated and are never counted); they are right whenever the
+  // prompt has more than three tiles, and are redone otherwise.
   const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
                         ((int64_t)r * p.Hkv + k) * p.Lmax * D;
   const uint16_t *svg = static_cast<const uint16_t *>(p.shared_v) +
                         ((int64_t)r * p.Hkv + k) * p.Lmax * D;
   CopyPlan<D, WAVES> cplan;
   cplan.init(wave, lane);
+  const bool speculate = p.Lmax >= 3 * KT;
+  if (speculate) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      tile_copy<D, WAVES, false>(tiles + i * Gm::TILE_BYTES, tiles + (NSTAGE + i) * Gm::TILE_BYTES,
+                                 cplan, skg, svg, i * KT, 0, wave);
+  }
+  const int L = clampi(p.prompt_len[r], 0, p.Lmax);
+  const int n_tiles = (L + KT - 1) / KT;
   // Tile t covers keys [t*KT, t*KT + KT); the last one's window is shifted
   // back to [L - KT, L) (when L >= KT) so that no copy needs clamping; its
   // keys below (n_tiles - 1) * KT were already counted and get masked.
@@ -568,10 +621,14 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
 #define XATTN_KT(S) (tiles + (S) * Gm::TILE_BYTES)
 #define XATTN_VT(S) (tiles + (NSTAGE + (S)) * Gm::TILE_BYTES)
 #define XATTN_KEY0(T) ((T) + 1 < n_tiles ? (T) * KT : last_key0)
-  if (L < KT) {
+  if (speculate && n_tiles > 3) {
+    // the speculative copies are tiles 0, 1, 2
+  } else if (L < KT) {
+    if (speculate) wait_vm_lgkm0<0>();  // this wave's copies into the stages have landed
     if (n_tiles > 0)
       tile_copy<D, WAVES, true>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, 0, L, wave);
   } else {
+    if (speculate) wait_vm_lgkm0<0>();
     tile_copy<D, WAVES, false>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, XATTN_KEY0(0), L, wave);
     if (n_tiles > 1)
       tile_copy<D, WAVES, false>(XATTN_KT(1), XATTN_VT(1), cplan, skg, svg, XATTN_KEY0(1), L,
@@ -603,6 +660,21 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     }
   }
 
+  // ---- Unshared stage, while the first tiles are in flight (its later
+  // loads are younger than the copies, so waiting for them waits for the
+  // copies too; the debug variant runs the stage on its own after the merge
+  // of the key halves).  Key half kh takes levels step - kh, step - kh - 2,
+  // ...  Its state seeds the online softmax the shared tiles continue.
+  Rows<D> st;
+  st.clear();
+  const int32_t *anc_row = anc_lds + (beam - b_lo) * (step + 1);
+  const int64_t anc_ws_base = (int64_t)r * (step + 1) * BW + beam;
+  if constexpr (!TAPS) {
+    if (walk_here) lds_barrier();  // every beam's slots are in LDS
+    unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step - kh, KSPLIT, c,
+                       lane, cur_tok, early_tok);
+  }
+
   // ---- Shared stage.  Per tile t (in stage t % NSTAGE) but the last: wait
   // for tile t + 1 and synchronise, start the copy of tile t + 3 into the
   // stage tile t - 1 used, finish the row maxima of tile t, then issue the
@@ -610,8 +682,6 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // matrix cores and the VALU work side by side), then tile t's PV MFMAs.
   FragOffsets<D> fo;
   fo.init(kh, NKB, lane);
-  Rows<D> st;
-  st.clear();
   f32x16 s_cur[NKB], s_next[NKB];
   bf16x8 pf[2 * NKB];
   if (n_tiles > 0) {
@@ -636,14 +706,14 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     else                                                                              \
       wait_vm_lgkm0<0>();                                                             \
     lds_barrier();                                                                    \
-    if (t + 3 < n_tiles)                                                              \
-      tile_copy<D, WAVES, false>(XATTN_KT(((ST) + 3) % NSTAGE),                       \
-                                 XATTN_VT(((ST) + 3) % NSTAGE), cplan, skg, svg,      \
-                                 XATTN_KEY0(t + 3), L, wave);                         \
     const float mc = softmax_max<D, KSPLIT, false>(s_cur, st, kh, 0, 0, L, c, thr, lane); \
     qk_next_with_exp<D, KSPLIT>(XATTN_KT(((ST) + 1) % NSTAGE), qf, s_next, s_cur, pf, st, \
                                 c, mc, fo);                                           \
     pv_tile<D, KSPLIT>(XATTN_VT(ST), pf, st, kh, fo);                                 \
+    if (t + 3 < n_tiles)                                                              \
+      tile_copy<D, WAVES, false>(XATTN_KT(((ST) + 3) % NSTAGE),                       \
+                                 XATTN_VT(((ST) + 3) % NSTAGE), cplan, skg, svg,      \
+                                 XATTN_KEY0(t + 3), L, wave);                         \
     _Pragma("unroll") for (int i = 0; i < NKB; ++i) s_cur[i] = s_next[i];             \
   }
   static_assert(NSTAGE == 4, "the tile loop below is unrolled for 4 stages");
@@ -667,19 +737,6 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   }
 #undef XATTN_KEY0
 
-  // ---- Unshared stage (all copies have landed; its loads queue behind
-  // nothing).  Key halves take alternate levels; the debug variant keeps
-  // the stage on its own in key half 0, after the halves are merged.
-  const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
-                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
-  const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
-                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
-  const int32_t *anc_row = anc_lds + (beam - b_lo) * (step + 1);
-  const int64_t anc_ws_base = (int64_t)r * (step + 1) * BW + beam;
-  if constexpr (!TAPS)
-    unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step, kh, KSPLIT, c,
-                       lane);
-
   // ---- the second key half hands its state to the first through LDS
   // (stage buffer rg holds row group rg's exchange)
   if constexpr (KSPLIT == 2) {
@@ -687,13 +744,15 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     static_assert(NDB * 16 * 64 * 4 <= Gm::TILE_BYTES, "the exchanged O must fit a K tile");
     wait_vm_lgkm0<0>();
     lds_barrier();  // every wave is done with the tile stages
-    float *xo = reinterpret_cast<float *>(XATTN_KT(rg));   // O
-    float *xs = reinterpret_cast<float *>(XATTN_VT(rg));   // m, l
+    float4 *xo = reinterpret_cast<float4 *>(XATTN_KT(rg));   // O, 16 B per lane and step
+    float *xs = reinterpret_cast<float *>(XATTN_VT(rg));     // m, l
     if (kh == 1) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) xo[(db * 16 + e) * 64 + lane] = st.O[db][e];
+        for (int j = 0; j < 4; ++j)
+          xo[(db * 4 + j) * 64 + lane] = make_float4(st.O[db][4 * j], st.O[db][4 * j + 1],
+                                                     st.O[db][4 * j + 2], st.O[db][4 * j + 3]);
       xs[lane] = st.m;
       xs[64 + lane] = st.l;
     }
@@ -713,8 +772,13 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        st.O[db][e] = st.O[db][e] * a1 + xo[(db * 16 + e) * 64 + lane] * a2;
+      for (int j = 0; j < 4; ++j) {
+        const float4 o2 = xo[(db * 4 + j) * 64 + lane];
+        st.O[db][4 * j + 0] = st.O[db][4 * j + 0] * a1 + o2.x * a2;
+        st.O[db][4 * j + 1] = st.O[db][4 * j + 1] * a1 + o2.y * a2;
+        st.O[db][4 * j + 2] = st.O[db][4 * j + 2] * a1 + o2.z * a2;
+        st.O[db][4 * j + 3] = st.O[db][4 * j + 3] * a1 + o2.w * a2;
+      }
   }
 #undef XATTN_KT
 #undef XATTN_VT
@@ -727,7 +791,9 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     // own; then their explicit OnlineSoftmax merge.
     Rows<D> su;
     su.clear();
-    unshared_tokens<D>(su, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step, 0, 1, c, lane);
+    TokenRows<D> su_none;
+    unshared_tokens<D>(su, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step, 1, c, lane,
+                       su_none, false);
     const float ls = pair_sum(st.l), lu = pair_sum(su.l);
     const float ms = st.m, mu = su.m;
     const float inv_s = ls > 0.f ? 1.f / ls : 0.f;
