@@ -58,18 +58,6 @@ constexpr int NSTAGE = 4;   // LDS ring depth (tiles in flight = NSTAGE - 1)
 __device__ inline float lo_bf16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ inline float hi_bf16(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-__device__ inline float dot8(uint4 a, uint4 b, float acc) {
-  acc = fmaf(lo_bf16(a.x), lo_bf16(b.x), acc);
-  acc = fmaf(hi_bf16(a.x), hi_bf16(b.x), acc);
-  acc = fmaf(lo_bf16(a.y), lo_bf16(b.y), acc);
-  acc = fmaf(hi_bf16(a.y), hi_bf16(b.y), acc);
-  acc = fmaf(lo_bf16(a.z), lo_bf16(b.z), acc);
-  acc = fmaf(hi_bf16(a.z), hi_bf16(b.z), acc);
-  acc = fmaf(lo_bf16(a.w), lo_bf16(b.w), acc);
-  acc = fmaf(hi_bf16(a.w), hi_bf16(b.w), acc);
-  return acc;
-}
-
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -448,15 +436,23 @@ __device__ __forceinline__ void load_token(TokenRows<D> &tr, const uint16_t *ukg
       tr.vr[db][j] = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
 }
 
-// Online-softmax update of a row's state with one token (fp32 dot product
-// on the VALU; the pair of lanes holding the row adds its two halves).
+// Online-softmax update of a row's state with one token (dot product on
+// the VALU, bf16 pairs into fp32; the pair of lanes holding the row adds
+// its two halves).
 template <int D>
 __device__ __forceinline__ void add_token(Rows<D> &st, const bf16x8 (&qf)[D / 16],
                                           const TokenRows<D> &tr, float c, int hl) {
   float part = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    part = dot8(__builtin_bit_cast(uint4, qf[ks]), tr.kr[ks], part);
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const uint4 kw = tr.kr[ks];
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 qa = {qf[ks][2 * e], qf[ks][2 * e + 1]};
+      part = __builtin_amdgcn_fdot2_f32_bf16(qa, __builtin_bit_cast(bf16x2, kk[e]), part, false);
+    }
+  }
   const float sc = pair_sum(part);
   const float mn = fmaxf(st.m, sc);
   const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // 0 while m is -inf
@@ -494,6 +490,7 @@ __device__ __forceinline__ void unshared_tokens(Rows<D> &st, const bf16x8 (&qf)[
     t_first -= t_stride;
   }
   TokenRows<D> tr;
+#pragma unroll 1
   for (int t = t_first; t >= 0; t -= t_stride) {
     const int slot =
         anc_ws ? clampi(anc_ws[anc_ws_base + (int64_t)t * BW], 0, BW - 1) : anc_row[t];
@@ -505,6 +502,107 @@ __device__ __forceinline__ void unshared_tokens(Rows<D> &st, const bf16x8 (&qf)[
 // Parent rows of levels 1..step are staged in LDS for the ancestor walk
 // when they fit this many ints; longer chains are resolved beforehand into
 // the workspace.
+// Generated-token rows of a row block, gathered into LDS in the layout of
+// the prompt tiles: token i of the sequence is (level i / nb, block beam
+// i % nb), for levels 0..step; a gathered tile holds tokens tok0, tok0 + 1,
+// ... in its rows.  Each row's source is the token row of that beam's
+// ancestor slot at that level (anc_lds [nb][step + 1]).  Rows past the last
+// token repeat it (their data is never read).  The KT-row tiles use the
+// prompt tiles' copy plan.
+template <int D>
+__device__ __forceinline__ void token_row_copy(uint8_t *dst, const uint16_t *base_g, int row,
+                                               uint32_t slot_off, int tok0, int n_tok, int nb,
+                                               int BW, const int32_t *anc_lds, int step) {
+  using Gm = TileGeom<D>;
+  const int tok = min(tok0 + row, n_tok - 1);
+  const int lvl = tok / nb;
+  const int bi = tok - lvl * nb;
+  const int slot = anc_lds[bi * (step + 1) + lvl];
+  const uint8_t *src = reinterpret_cast<const uint8_t *>(base_g) +
+                       ((int64_t)lvl * BW + slot) * Gm::RB + slot_off;
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
+                                   (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
+
+template <int D, int WAVES>
+__device__ __forceinline__ void token_copy(uint8_t *ktile, uint8_t *vtile,
+                                           const CopyPlan<D, WAVES> &cp, const uint16_t *ukg,
+                                           const uint16_t *uvg, int tok0, int n_tok, int nb,
+                                           int BW, const int32_t *anc_lds, int step, int wave) {
+  using Gm = TileGeom<D>;
+  using C = CopyPlan<D, WAVES>;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int qi = wave * C::PER + i;
+    const bool is_v = qi >= C::NQ;
+    const int q = is_v ? qi - C::NQ : qi;
+    const int row = C::row_of(cp.off[i]);
+    token_row_copy<D>((is_v ? vtile : ktile) + q * 1024, is_v ? uvg : ukg, row,
+                      cp.off[i] - (uint32_t)(row * Gm::RB), tok0, n_tok, nb, BW, anc_lds, step);
+  }
+}
+
+// The first SPARE tokens go to a region of their own (SPARE rows of K,
+// then of V), copied as soon as the ancestor slots are known.
+constexpr int kSpareRows = 32;
+
+template <int D, int WAVES>
+__device__ __forceinline__ void spare_copy(uint8_t *sk, uint8_t *sv, const uint16_t *ukg,
+                                           const uint16_t *uvg, int n_tok, int nb, int BW,
+                                           const int32_t *anc_lds, int step, int wave, int lane) {
+  using Gm = TileGeom<D>;
+  constexpr int NQ = kSpareRows * Gm::RB / 1024;  // 1 KiB copies per K (or V) region
+  static_assert((2 * NQ) % WAVES == 0, "spare copies must split evenly over the waves");
+  constexpr int PER = 2 * NQ / WAVES;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int qi = wave * PER + i;
+    const bool is_v = qi >= NQ;
+    const int q = is_v ? qi - NQ : qi;
+    const int row = q * Gm::ROWS_PER_COPY + lane / Gm::SLOTS;
+    const uint32_t slot_off = (uint32_t)(((lane % Gm::SLOTS) ^ Gm::swz(row)) << 4);
+    token_row_copy<D>((is_v ? sv : sk) + q * 1024, is_v ? uvg : ukg, row, slot_off, 0, n_tok, nb,
+                      BW, anc_lds, step);
+  }
+}
+// One token row from a gathered LDS tile, in the lanes' TokenRows layout
+// (global 16-byte slot g of row `row` sits at LDS slot g ^ swz(row)).
+template <int D>
+__device__ __forceinline__ void lds_token(TokenRows<D> &tr, const uint8_t *kt, const uint8_t *vt,
+                                          int row, int hl) {
+  using Gm = TileGeom<D>;
+  const int sw = Gm::swz(row);
+  const uint8_t *kr = kt + row * Gm::RB;
+  const uint8_t *vr = vt + row * Gm::RB;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    tr.kr[ks] = *reinterpret_cast<const uint4 *>(kr + (((2 * ks + hl) ^ sw) << 4));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      tr.vr[db][j] = *reinterpret_cast<const uint2 *>(vr + (((4 * db + j) ^ sw) << 4) + 8 * hl);
+}
+
+// Unshared stage over one gathered tile holding tokens [i_lo, i_hi): the
+// tokens of this lane's beam `bi` among them, key half kh taking the levels
+// congruent to kh modulo KSPLIT.
+template <int D, int KSPLIT>
+__device__ __forceinline__ void unshared_chunk(Rows<D> &st, const bf16x8 (&qf)[D / 16],
+                                               const uint8_t *kt, const uint8_t *vt, int i_lo,
+                                               int i_hi, int nb, int bi, int kh, float c,
+                                               int lane) {
+  const int hl = lane >> 5;
+  int lvl = (i_lo - bi + nb - 1) / nb;   // first level whose row is in this tile
+  lvl += (kh - lvl % KSPLIT + KSPLIT) % KSPLIT;
+  TokenRows<D> tr;
+#pragma unroll 1
+  for (; lvl * nb + bi < i_hi; lvl += KSPLIT) {
+    lds_token<D>(tr, kt, vt, lvl * nb + bi - i_lo, hl);
+    add_token<D>(st, qf, tr, c, hl);
+  }
+}
+
 constexpr int kParentLdsInts = 2048;
 
 __host__ __device__ inline bool stage_parents_in_lds(int step, int BW) {
@@ -528,7 +626,9 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // fragment address be a per-lane register plus an immediate, and let the
   // compiler see that a copy into one stage does not alias reads of
   // another (so it adds no wait of its own in front of those reads).
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * NSTAGE * Gm::TILE_BYTES];
+  // After the ring, the first generated-token rows (K, then V).
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t tiles[2 * NSTAGE * Gm::TILE_BYTES + 2 * kSpareRows * Gm::RB];
   // dynamic: ancestor slots [beams of the block][step + 1], then (when
   // staged) the parent rows [step][BW] of levels 1..step
   extern __shared__ int32_t dyn_lds[];
@@ -584,15 +684,10 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     qf[ks] = __builtin_bit_cast(bf16x8,
                                 *reinterpret_cast<const uint4 *>(qg + qoff + ks * 16 + hl * 8));
 
-  // ---- the current level's token rows (its slot is the beam itself, so no
-  // ancestor is needed): key half 0 starts them now
   const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
                         ((int64_t)r * p.Hkv + k) * p.S * BW * D;
   const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
                         ((int64_t)r * p.Hkv + k) * p.S * BW * D;
-  TokenRows<D> cur_tok;
-  const bool early_tok = !TAPS && kh == 0;
-  if (early_tok) load_token<D>(cur_tok, ukg, uvg, ((int64_t)step * BW + beam) * D, hl);
 
   // ---- start the tile pipeline: tiles 0 .. NSTAGE-2 in flight.  When the
   // cache holds at least three tiles of rows, the copies of keys [0, 3 KT)
@@ -638,7 +733,25 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
                                  wave);
   }
 
-  // ---- ancestor slots of the block's beams (short chains: walked here)
+  // ---- generated-token rows.  With the ancestor slots in LDS they are
+  // gathered into LDS: the first kSpareRows tokens into a region of their
+  // own as soon as the slots are known, the rest in KT-row tiles
+  // ("chunks").  Chunk j is copied at loop step chunk_t0 + j into the stage
+  // that step frees, in the last two steps, where no prompt tile remains to
+  // copy, so it lands while the last prompt tiles are consumed; chunks
+  // that find no such step are copied after the loop.  Deep chains (slots
+  // in the workspace) read their rows directly.
+  const bool lds_tokens = !TAPS && walk_here;
+  const int n_tok = (step + 1) * nb;
+  const int n_chunks = lds_tokens ? (max(n_tok - kSpareRows, 0) + KT - 1) / KT : 0;
+  const int chunk_t0 = max(0, n_tiles - 3);
+#define XATTN_SK (tiles + 2 * NSTAGE * Gm::TILE_BYTES)
+#define XATTN_SV (tiles + 2 * NSTAGE * Gm::TILE_BYTES + kSpareRows * Gm::RB)
+
+  // ---- wait for tiles 0..2, the parent rows and q, then the ancestor
+  // slots of the block's beams (short chains: walked here, from the parent
+  // rows staged in LDS)
+  wait_vm_lgkm0<0>();
   if (staged) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -659,49 +772,44 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       }
     }
   }
+  lds_barrier();  // tile 0 and the ancestor slots are visible
+  if (lds_tokens)
+    spare_copy<D, WAVES>(XATTN_SK, XATTN_SV, ukg, uvg, n_tok, nb, BW, anc_lds, step, wave, lane);
 
-  // ---- Unshared stage, while the first tiles are in flight (its later
-  // loads are younger than the copies, so waiting for them waits for the
-  // copies too; the debug variant runs the stage on its own after the merge
-  // of the key halves).  Key half kh takes levels step - kh, step - kh - 2,
-  // ...  Its state seeds the online softmax the shared tiles continue.
   Rows<D> st;
   st.clear();
   const int32_t *anc_row = anc_lds + (beam - b_lo) * (step + 1);
   const int64_t anc_ws_base = (int64_t)r * (step + 1) * BW + beam;
   if constexpr (!TAPS) {
-    if (walk_here) lds_barrier();  // every beam's slots are in LDS
-    unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step - kh, KSPLIT, c,
-                       lane, cur_tok, early_tok);
+    // deep chains: key half kh takes levels step - kh, step - kh - 2, ...;
+    // the state seeds the online softmax the prompt tiles continue
+    if (!walk_here) {
+      TokenRows<D> none;
+      unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step - kh, KSPLIT,
+                         c, lane, none, false);
+    }
   }
 
   // ---- Shared stage.  Per tile t (in stage t % NSTAGE) but the last: wait
-  // for tile t + 1 and synchronise, start the copy of tile t + 3 into the
-  // stage tile t - 1 used, finish the row maxima of tile t, then issue the
-  // S^T MFMAs of tile t + 1 interleaved with the exponentials of tile t (the
-  // matrix cores and the VALU work side by side), then tile t's PV MFMAs.
+  // for tile t + 1 and synchronise, finish the row maxima of tile t, then
+  // issue the S^T MFMAs of tile t + 1 interleaved with the exponentials of
+  // tile t (the matrix cores and the VALU work side by side), then tile t's
+  // PV MFMAs, then copy tile t + 3 (or a token chunk) into the stage tile
+  // t - 1 used.
   FragOffsets<D> fo;
   fo.init(kh, NKB, lane);
   f32x16 s_cur[NKB], s_next[NKB];
   bf16x8 pf[2 * NKB];
-  if (n_tiles > 0) {
-    if (n_tiles > 2)
-      wait_vm_lgkm0<2 * CPW>();
-    else if (n_tiles > 1)
-      wait_vm_lgkm0<CPW>();
-    else
-      wait_vm_lgkm0<0>();
-    lds_barrier();  // tile 0 and the ancestor slots are visible
-    qk_tile<D, KSPLIT>(XATTN_KT(0), qf, s_cur, fo);
-  } else {
-    wait_vm_lgkm0<63>();
-    lds_barrier();  // the ancestor slots are visible
-  }
+  if (n_tiles > 0) qk_tile<D, KSPLIT>(XATTN_KT(0), qf, s_cur, fo);
 #define XATTN_TILE_STEP(ST)                                                           \
   {                                                                                   \
     const int t = t0 + (ST);                                                          \
     if (t + 1 >= n_tiles) break;                                                      \
-    if (t + 2 < n_tiles)                                                              \
+    /* tiles 1 and 2 came in before the loop; tile t + 1 > 2 is in once */          \
+    /* everything but the copy of step t - 1 (tile t + 2 or a chunk) is */            \
+    if (t < 2)                                                                        \
+      wait_vm_lgkm0<63>();                                                            \
+    else if (t + 2 < n_tiles || (t - 1 >= chunk_t0 && t - 1 - chunk_t0 < n_chunks))  \
       wait_vm_lgkm0<CPW>();                                                           \
     else                                                                              \
       wait_vm_lgkm0<0>();                                                             \
@@ -714,6 +822,10 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       tile_copy<D, WAVES, false>(XATTN_KT(((ST) + 3) % NSTAGE),                       \
                                  XATTN_VT(((ST) + 3) % NSTAGE), cplan, skg, svg,      \
                                  XATTN_KEY0(t + 3), L, wave);                         \
+    else if (t >= chunk_t0 && t - chunk_t0 < n_chunks)                                \
+      token_copy<D, WAVES>(XATTN_KT(((ST) + 3) % NSTAGE), XATTN_VT(((ST) + 3) % NSTAGE), \
+                           cplan, ukg, uvg, kSpareRows + (t - chunk_t0) * KT, n_tok, nb, BW,    \
+                           anc_lds, step, wave);                                      \
     _Pragma("unroll") for (int i = 0; i < NKB; ++i) s_cur[i] = s_next[i];             \
   }
   static_assert(NSTAGE == 4, "the tile loop below is unrolled for 4 stages");
@@ -736,6 +848,40 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     pv_tile<D, KSPLIT>(tiles + (NSTAGE + t % NSTAGE) * Gm::TILE_BYTES, pf, st, kh, fo);
   }
 #undef XATTN_KEY0
+
+  // ---- Unshared stage from the gathered token rows: the first ones, the
+  // chunks copied in the loop (chunk j in stage (chunk_t0 + j + 3) %
+  // NSTAGE), then any others one at a time through stage 0
+  if constexpr (!TAPS) {
+    if (lds_tokens) {
+      const int bi = beam - b_lo;
+      const int n_pref = min(n_chunks, max(0, n_tiles - 1 - chunk_t0));
+      wait_vm_lgkm0<0>();
+      lds_barrier();  // the tokens are in; every wave is done with the prompt tiles
+      unshared_chunk<D, KSPLIT>(st, qf, XATTN_SK, XATTN_SV, 0, min(n_tok, kSpareRows), nb, bi, kh,
+                                c, lane);
+#pragma unroll 1
+      for (int j = 0; j < n_pref; ++j) {
+        const int sg = (chunk_t0 + j + 3) % NSTAGE;
+        const int i0 = kSpareRows + j * KT;
+        unshared_chunk<D, KSPLIT>(st, qf, XATTN_KT(sg), XATTN_VT(sg), i0, min(n_tok, i0 + KT), nb,
+                                  bi, kh, c, lane);
+      }
+#pragma unroll 1
+      for (int j = n_pref; j < n_chunks; ++j) {
+        const int i0 = kSpareRows + j * KT;
+        lds_barrier();  // no wave still reads stage 0
+        token_copy<D, WAVES>(XATTN_KT(0), XATTN_VT(0), cplan, ukg, uvg, i0, n_tok, nb, BW,
+                             anc_lds, step, wave);
+        wait_vm_lgkm0<0>();
+        lds_barrier();
+        unshared_chunk<D, KSPLIT>(st, qf, XATTN_KT(0), XATTN_VT(0), i0, min(n_tok, i0 + KT), nb,
+                                  bi, kh, c, lane);
+      }
+    }
+  }
+#undef XATTN_SK
+#undef XATTN_SV
 
   // ---- the second key half hands its state to the first through LDS
   // (stage buffer rg holds row group rg's exchange)
