@@ -108,6 +108,28 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
 }
 
+// One wave-wide 16-byte-per-lane copy global -> LDS (global_load_lds): lane
+// i's 16 bytes at src land at LDS byte address lds_base + 16 i.  Issued as
+// inline asm so that the compiler does not see the LDS write: it would
+// otherwise put a full vmcnt(0) wait in front of LDS reads it cannot prove
+// disjoint from copies in flight (the transposing V reads carry no alias
+// information), draining the tile pipeline.  Every use of copied data is
+// preceded by an explicit vmcnt wait and a barrier; the copy counts in vmcnt
+// like any load, in issue order.
+__device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  uint32_t saved;  // M0 is the compiler's: put it back
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+}
+
 // Workgroup barrier that also orders this wave's LDS accesses in the
 // compiler, without the vmcnt(0) a full fence would impose on the tile
 // copies still in flight.  Callers wait for the copies they need first.
@@ -192,8 +214,7 @@ __device__ __forceinline__ void tile_copy(uint8_t *ktile, uint8_t *vtile,
       src = base + (int64_t)key * Gm::RB + (cp.off[i] - (uint32_t)(row * Gm::RB));
     }
     uint8_t *dst = (is_v ? vtile : ktile) + q * 1024;
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    dma16(src, dst);
   }
 }
 
@@ -289,8 +310,10 @@ __device__ __forceinline__ float softmax_max(f32x16 (&sacc)[2 / KSPLIT], Rows<D>
   }
   tmax = pair_max(tmax);
   if (__any(tmax > st.m + thr)) {
+    // masks may differ between rows (token blocks): a row that has seen no
+    // key yet and sees none here keeps m = -inf and its zero state
     const float mn = fmaxf(st.m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);
+    const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((st.m - mn) * c);
     st.m = mn;
     st.l *= alpha;
 #pragma unroll
@@ -503,32 +526,73 @@ __device__ __forceinline__ void unshared_tokens(Rows<D> &st, const bf16x8 (&qf)[
 // when they fit this many ints; longer chains are resolved beforehand into
 // the workspace.
 // Generated-token rows of a row block, gathered into LDS in the layout of
-// the prompt tiles: token i of the sequence is (level i / nb, block beam
-// i % nb), for levels 0..step; a gathered tile holds tokens tok0, tok0 + 1,
-// ... in its rows.  Each row's source is the token row of that beam's
-// ancestor slot at that level (anc_lds [nb][step + 1]).  Rows past the last
-// token repeat it (their data is never read).  The KT-row tiles use the
-// prompt tiles' copy plan.
-template <int D>
-__device__ __forceinline__ void token_row_copy(uint8_t *dst, const uint16_t *base_g, int row,
-                                               uint32_t slot_off, int tok0, int n_tok, int nb,
-                                               int BW, const int32_t *anc_lds, int step) {
-  using Gm = TileGeom<D>;
-  const int tok = min(tok0 + row, n_tok - 1);
-  const int lvl = tok / nb;
-  const int bi = tok - lvl * nb;
-  const int slot = anc_lds[bi * (step + 1) + lvl];
-  const uint8_t *src = reinterpret_cast<const uint8_t *>(base_g) +
-                       ((int64_t)lvl * BW + slot) * Gm::RB + slot_off;
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)src,
-                                   (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-}
+// the prompt tiles, in blocks of 32 rows.  Row group g of the block has
+// n_blk blocks; block b of it holds its tokens 32 b .. 32 b + 31, token i
+// being (beam first(g) + i / nlev, level i % nlev), nlev = step + 1, where
+// first(g) is the beam of the group's first query row.  Blocks are
+// numbered gb = b * RG + g.  A row's source is the token row of its beam's
+// ancestor slot at its level (anc_lds [nb][step + 1], indexed from the row
+// block's first beam b_lo); rows past a group's tokens repeat a valid row
+// (their scores are masked).
+template <int RG>
+struct TokenMap {
+  const int32_t *anc_lds;
+  int n_blk, nlev, BW, nb;
+  // i / nlev == (i * nlev_magic) >> 20 for the token counts used here
+  // (i * nlev < 2^20), nlev_magic = floor(2^20 / nlev) + 1
+  uint32_t nlev_magic;
+  int first[RG];   // first beam of each row group, from the row block's first beam
+  __device__ void init(const int32_t *anc, int n_blk_, int nlev_, int BW_, int nb_, int G,
+                       int row0, int b_lo) {
+    anc_lds = anc;
+    n_blk = n_blk_;
+    nlev = nlev_;
+    BW = BW_;
+    nb = nb_;
+    nlev_magic = (1u << 20) / (uint32_t)nlev_ + 1u;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) first[g] = (row0 + 32 * g) / G - b_lo;
+  }
+  // row index (level * BW + slot) of row r of block gb in the (request, KV
+  // head) slice of the unshared cache
+  __device__ int row_index(int gb, int r) const {
+    gb = min(gb, RG * n_blk - 1);
+    const int g = gb % RG, b = gb / RG;
+    const int i = 32 * b + r;
+    const int jb = (int)(((uint32_t)i * nlev_magic) >> 20);
+    const int lvl = i - jb * nlev;
+    int f = first[0];
+#pragma unroll
+    for (int k = 1; k < RG; ++k) f = g == k ? first[k] : f;
+    const int bi = clampi(f + jb, 0, nb - 1);
+    return lvl * BW + anc_lds[bi * nlev + lvl];
+  }
+  // element offset of row r of block gb in the (request, KV head) slice
+  __device__ int64_t row_elem(int gb, int r, int D) const {
+    gb = min(gb, RG * n_blk - 1);
+    const int g = gb % RG, b = gb / RG;
+    const int i = 32 * b + r;
+    const int jb = (int)(((uint32_t)i * nlev_magic) >> 20);
+    const int lvl = i - jb * nlev;
+    int f = first[0];
+#pragma unroll
+    for (int k = 1; k < RG; ++k) f = g == k ? first[k] : f;
+    const int bi = clampi(f + jb, 0, nb - 1);
+    const int slot = anc_lds[bi * nlev + lvl];
+    return ((int64_t)lvl * BW + slot) * D;
+  }
+};
 
+// Blocks 1 + 2c and 2 + 2c as one KT-row tile (chunk c), with the prompt
+// tiles' copy plan; rows[i] is the row index of copy i's row (TokenMap::
+// row_index), read from registers so that no LDS read sits between the
+// copies in flight and this one.
 template <int D, int WAVES>
-__device__ __forceinline__ void token_copy(uint8_t *ktile, uint8_t *vtile,
-                                           const CopyPlan<D, WAVES> &cp, const uint16_t *ukg,
-                                           const uint16_t *uvg, int tok0, int n_tok, int nb,
-                                           int BW, const int32_t *anc_lds, int step, int wave) {
+__device__ __forceinline__ void token_chunk_copy_rows(uint8_t *ktile, uint8_t *vtile,
+                                                      const CopyPlan<D, WAVES> &cp,
+                                                      const uint16_t *ukg, const uint16_t *uvg,
+                                                      const int (&rows)[CopyPlan<D, WAVES>::PER],
+                                                      int wave) {
   using Gm = TileGeom<D>;
   using C = CopyPlan<D, WAVES>;
 #pragma unroll
@@ -537,22 +601,46 @@ __device__ __forceinline__ void token_copy(uint8_t *ktile, uint8_t *vtile,
     const bool is_v = qi >= C::NQ;
     const int q = is_v ? qi - C::NQ : qi;
     const int row = C::row_of(cp.off[i]);
-    token_row_copy<D>((is_v ? vtile : ktile) + q * 1024, is_v ? uvg : ukg, row,
-                      cp.off[i] - (uint32_t)(row * Gm::RB), tok0, n_tok, nb, BW, anc_lds, step);
+    const uint8_t *src = reinterpret_cast<const uint8_t *>((is_v ? uvg : ukg) + (int64_t)rows[i] * D) +
+                         (cp.off[i] - (uint32_t)(row * Gm::RB));
+    dma16(src, ((is_v ? vtile : ktile) + q * 1024));
   }
 }
 
-// The first SPARE tokens go to a region of their own (SPARE rows of K,
-// then of V), copied as soon as the ancestor slots are known.
-constexpr int kSpareRows = 32;
-
-template <int D, int WAVES>
-__device__ __forceinline__ void spare_copy(uint8_t *sk, uint8_t *sv, const uint16_t *ukg,
-                                           const uint16_t *uvg, int n_tok, int nb, int BW,
-                                           const int32_t *anc_lds, int step, int wave, int lane) {
+// Blocks 1 + 2c and 2 + 2c as one KT-row tile (chunk c), with the prompt
+// tiles' copy plan.
+template <int D, int WAVES, int RG>
+__device__ __forceinline__ void token_chunk_copy(uint8_t *ktile, uint8_t *vtile,
+                                                 const CopyPlan<D, WAVES> &cp,
+                                                 const uint16_t *ukg, const uint16_t *uvg,
+                                                 const TokenMap<RG> &tm, int chunk, int wave) {
   using Gm = TileGeom<D>;
-  constexpr int NQ = kSpareRows * Gm::RB / 1024;  // 1 KiB copies per K (or V) region
-  static_assert((2 * NQ) % WAVES == 0, "spare copies must split evenly over the waves");
+  using C = CopyPlan<D, WAVES>;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int qi = wave * C::PER + i;
+    const bool is_v = qi >= C::NQ;
+    const int q = is_v ? qi - C::NQ : qi;
+    const int row = C::row_of(cp.off[i]);
+    const int64_t e = tm.row_elem(1 + 2 * chunk + row / 32, row % 32, D);
+    const uint8_t *src = reinterpret_cast<const uint8_t *>((is_v ? uvg : ukg) + e) +
+                         (cp.off[i] - (uint32_t)(row * Gm::RB));
+    dma16(src, ((is_v ? vtile : ktile) + q * 1024));
+  }
+}
+
+// Wave-wide copies per wave that token_block0_copy issues.
+template <int D, int WAVES>
+constexpr int block0_copies_per_wave() { return 2 * (32 * TileGeom<D>::RB / 1024) / WAVES; }
+
+// Block 0 into its own region (32 rows of K at sk, of V at sv).
+template <int D, int WAVES, int RG>
+__device__ __forceinline__ void token_block0_copy(uint8_t *sk, uint8_t *sv, const uint16_t *ukg,
+                                                  const uint16_t *uvg, const TokenMap<RG> &tm,
+                                                  int wave, int lane) {
+  using Gm = TileGeom<D>;
+  constexpr int NQ = 32 * Gm::RB / 1024;  // 1 KiB copies per K (or V) block
+  static_assert((2 * NQ) % WAVES == 0, "block copies must split evenly over the waves");
   constexpr int PER = 2 * NQ / WAVES;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -560,47 +648,41 @@ __device__ __forceinline__ void spare_copy(uint8_t *sk, uint8_t *sv, const uint1
     const bool is_v = qi >= NQ;
     const int q = is_v ? qi - NQ : qi;
     const int row = q * Gm::ROWS_PER_COPY + lane / Gm::SLOTS;
-    const uint32_t slot_off = (uint32_t)(((lane % Gm::SLOTS) ^ Gm::swz(row)) << 4);
-    token_row_copy<D>((is_v ? sv : sk) + q * 1024, is_v ? uvg : ukg, row, slot_off, 0, n_tok, nb,
-                      BW, anc_lds, step);
+    const int64_t e = tm.row_elem(0, row, D);
+    const uint8_t *src = reinterpret_cast<const uint8_t *>((is_v ? uvg : ukg) + e) +
+                         (((lane % Gm::SLOTS) ^ Gm::swz(row)) << 4);
+    dma16(src, ((is_v ? sv : sk) + q * 1024));
   }
-}
-// One token row from a gathered LDS tile, in the lanes' TokenRows layout
-// (global 16-byte slot g of row `row` sits at LDS slot g ^ swz(row)).
-template <int D>
-__device__ __forceinline__ void lds_token(TokenRows<D> &tr, const uint8_t *kt, const uint8_t *vt,
-                                          int row, int hl) {
-  using Gm = TileGeom<D>;
-  const int sw = Gm::swz(row);
-  const uint8_t *kr = kt + row * Gm::RB;
-  const uint8_t *vr = vt + row * Gm::RB;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    tr.kr[ks] = *reinterpret_cast<const uint4 *>(kr + (((2 * ks + hl) ^ sw) << 4));
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      tr.vr[db][j] = *reinterpret_cast<const uint2 *>(vr + (((4 * db + j) ^ sw) << 4) + 8 * hl);
 }
 
-// Unshared stage over one gathered tile holding tokens [i_lo, i_hi): the
-// tokens of this lane's beam `bi` among them, key half kh taking the levels
-// congruent to kh modulo KSPLIT.
+// Unshared stage on the matrix cores: one token block (rows at kt / vt, K
+// and V) against the wave's 32 query rows, as a 32-key tile whose scores
+// are masked block-diagonally: token i0 + i counts for a query row iff it
+// lies in [tok_lo, tok_hi), the row's own tokens (its beam's levels).
 template <int D, int KSPLIT>
-__device__ __forceinline__ void unshared_chunk(Rows<D> &st, const bf16x8 (&qf)[D / 16],
-                                               const uint8_t *kt, const uint8_t *vt, int i_lo,
-                                               int i_hi, int nb, int bi, int kh, float c,
-                                               int lane) {
+__device__ __forceinline__ void token_block(Rows<D> &st, const bf16x8 (&qf)[D / 16],
+                                            const uint8_t *kt, const uint8_t *vt,
+                                            const FragOffsets<D> &fo, int kh, int i0, int tok_lo,
+                                            int tok_hi, float c, float thr, int lane) {
+  static_assert(KSPLIT == 2, "a token block is one 32-key block per wave");
+  using Gm = TileGeom<D>;
   const int hl = lane >> 5;
-  int lvl = (i_lo - bi + nb - 1) / nb;   // first level whose row is in this tile
-  lvl += (kh - lvl % KSPLIT + KSPLIT) % KSPLIT;
-  TokenRows<D> tr;
-#pragma unroll 1
-  for (; lvl * nb + bi < i_hi; lvl += KSPLIT) {
-    lds_token<D>(tr, kt, vt, lvl * nb + bi - i_lo, hl);
-    add_token<D>(st, qf, tr, c, hl);
+  // the fragment offsets carry the key half's row offset: cancel it
+  const uint8_t *kb = kt - kh * 32 * Gm::RB;
+  const uint8_t *vb = vt - kh * 32 * Gm::RB;
+  f32x16 sb[1];
+  qk_tile<D, KSPLIT>(kb, qf, sb, fo);
+  const int base = i0 + 4 * hl - tok_lo;
+  const uint32_t span = (uint32_t)max(tok_hi - tok_lo, 0);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t d = (uint32_t)(base + 8 * (e / 4) + (e % 4));
+    sb[0][e] = d < span ? sb[0][e] : -INFINITY;
   }
+  bf16x8 pf[2];
+  const float mc = softmax_max<D, KSPLIT, false>(sb, st, kh, 0, 0, 0, c, thr, lane);
+  softmax_exp<D, KSPLIT>(sb, pf, st, c, mc);
+  pv_tile<D, KSPLIT>(vb, pf, st, kh, fo);
 }
 
 constexpr int kParentLdsInts = 2048;
@@ -626,9 +708,9 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // fragment address be a per-lane register plus an immediate, and let the
   // compiler see that a copy into one stage does not alias reads of
   // another (so it adds no wait of its own in front of those reads).
-  // After the ring, the first generated-token rows (K, then V).
+  // After the ring, token block 0 (32 rows of K, then of V).
   __shared__ __attribute__((aligned(1024)))
-  uint8_t tiles[2 * NSTAGE * Gm::TILE_BYTES + 2 * kSpareRows * Gm::RB];
+  uint8_t tiles[2 * NSTAGE * Gm::TILE_BYTES + 2 * 32 * Gm::RB];
   // dynamic: ancestor slots [beams of the block][step + 1], then (when
   // staged) the parent rows [step][BW] of levels 1..step
   extern __shared__ int32_t dyn_lds[];
@@ -734,24 +816,33 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   }
 
   // ---- generated-token rows.  With the ancestor slots in LDS they are
-  // gathered into LDS: the first kSpareRows tokens into a region of their
-  // own as soon as the slots are known, the rest in KT-row tiles
-  // ("chunks").  Chunk j is copied at loop step chunk_t0 + j into the stage
-  // that step frees, in the last two steps, where no prompt tile remains to
-  // copy, so it lands while the last prompt tiles are consumed; chunks
-  // that find no such step are copied after the loop.  Deep chains (slots
-  // in the workspace) read their rows directly.
+  // gathered into LDS in 32-row blocks (TokenMap): block 0 into a region of
+  // its own as soon as the slots are known, blocks 1 + 2c and 2 + 2c as
+  // chunk c, a KT-row tile.  Chunk c is copied at loop step chunk_t0 + c
+  // into the stage that step frees, in the last two steps, where no prompt
+  // tile remains to copy, so it lands while the last prompt tiles are
+  // consumed; chunks that find no such step are copied after the loop.
+  // Deep chains (slots in the workspace) read their rows directly.
   const bool lds_tokens = !TAPS && walk_here;
-  const int n_tok = (step + 1) * nb;
-  const int n_chunks = lds_tokens ? (max(n_tok - kSpareRows, 0) + KT - 1) / KT : 0;
+  const int nlev = step + 1;
+  const int nbr_max = (32 % G == 0) ? 32 / G : 32 / G + 2;  // beams 32 rows can touch
+  const int n_blk = (nbr_max * nlev + 31) / 32;
+  const int n_chunks = lds_tokens ? RG * n_blk / 2 : 0;
   const int chunk_t0 = max(0, n_tiles - 3);
+  TokenMap<RG> tmap;
+  tmap.init(anc_lds, n_blk, nlev, BW, nb, G, row0, b_lo);
 #define XATTN_SK (tiles + 2 * NSTAGE * Gm::TILE_BYTES)
-#define XATTN_SV (tiles + 2 * NSTAGE * Gm::TILE_BYTES + kSpareRows * Gm::RB)
+#define XATTN_SV (tiles + 2 * NSTAGE * Gm::TILE_BYTES + 32 * Gm::RB)
 
-  // ---- wait for tiles 0..2, the parent rows and q, then the ancestor
-  // slots of the block's beams (short chains: walked here, from the parent
-  // rows staged in LDS)
-  wait_vm_lgkm0<0>();
+  // ---- wait for tile 0 (the parent rows and q are older, so they are in
+  // too), then the ancestor slots of the block's beams (short chains:
+  // walked here, from the parent rows staged in LDS)
+  if (n_tiles > 2)
+    wait_vm_lgkm0<2 * CPW>();
+  else if (n_tiles > 1)
+    wait_vm_lgkm0<CPW>();
+  else
+    wait_vm_lgkm0<0>();
   if (staged) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
@@ -773,8 +864,20 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     }
   }
   lds_barrier();  // tile 0 and the ancestor slots are visible
-  if (lds_tokens)
-    spare_copy<D, WAVES>(XATTN_SK, XATTN_SV, ukg, uvg, n_tok, nb, BW, anc_lds, step, wave, lane);
+  // rows of the two chunks the loop may copy (the last two steps), read
+  // from LDS now, while no copy into LDS is in flight
+  constexpr int B0PW = block0_copies_per_wave<D, WAVES>();
+  int chunk_rows[2][CopyPlan<D, WAVES>::PER];
+  if (lds_tokens) {
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int i = 0; i < CopyPlan<D, WAVES>::PER; ++i) {
+        const int row = CopyPlan<D, WAVES>::row_of(cplan.off[i]);
+        chunk_rows[ch][i] = tmap.row_index(1 + 2 * ch + row / 32, row % 32);
+      }
+    token_block0_copy<D, WAVES>(XATTN_SK, XATTN_SV, ukg, uvg, tmap, wave, lane);
+  }
 
   Rows<D> st;
   st.clear();
@@ -801,18 +904,30 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   f32x16 s_cur[NKB], s_next[NKB];
   bf16x8 pf[2 * NKB];
   if (n_tiles > 0) qk_tile<D, KSPLIT>(XATTN_KT(0), qf, s_cur, fo);
+// whether step u's end copied something (tile u + 3, or chunk u - chunk_t0;
+// at most two chunks are copied in the loop)
+#define XATTN_COPIED(u) \
+  ((u) + 3 < n_tiles || ((u) >= chunk_t0 && (u) - chunk_t0 < n_chunks))
 #define XATTN_TILE_STEP(ST)                                                           \
   {                                                                                   \
     const int t = t0 + (ST);                                                          \
     if (t + 1 >= n_tiles) break;                                                      \
-    /* tiles 1 and 2 came in before the loop; tile t + 1 > 2 is in once */          \
-    /* everything but the copy of step t - 1 (tile t + 2 or a chunk) is */            \
-    if (t < 2)                                                                        \
-      wait_vm_lgkm0<63>();                                                            \
-    else if (t + 2 < n_tiles || (t - 1 >= chunk_t0 && t - 1 - chunk_t0 < n_chunks))  \
-      wait_vm_lgkm0<CPW>();                                                           \
-    else                                                                              \
-      wait_vm_lgkm0<0>();                                                             \
+    /* tile t + 1 is in once all but the copies younger than it are: the */        \
+    /* copy of step t - 1 (tile t + 2 or a chunk), and for t < 2 the */              \
+    /* prologue's tile 2 (t = 0) and block 0 */                                       \
+    {                                                                                 \
+      const bool cp_prev = t >= 1 && XATTN_COPIED(t - 1);                             \
+      const bool cp_more = t == 0 && n_tiles > 2;                                     \
+      const bool b0 = t < 2 && lds_tokens;                                            \
+      const int units = (cp_prev ? 1 : 0) + (cp_more ? 1 : 0);                        \
+      if (b0) {                                                                       \
+        if (units == 0) wait_vm_lgkm0<B0PW>();                                        \
+        else wait_vm_lgkm0<B0PW + CPW>();                                             \
+      } else {                                                                        \
+        if (units == 0) wait_vm_lgkm0<0>();                                           \
+        else wait_vm_lgkm0<CPW>();                                                    \
+      }                                                                               \
+    }                                                                                 \
     lds_barrier();                                                                    \
     const float mc = softmax_max<D, KSPLIT, false>(s_cur, st, kh, 0, 0, L, c, thr, lane); \
     qk_next_with_exp<D, KSPLIT>(XATTN_KT(((ST) + 1) % NSTAGE), qf, s_next, s_cur, pf, st, \
@@ -822,10 +937,10 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       tile_copy<D, WAVES, false>(XATTN_KT(((ST) + 3) % NSTAGE),                       \
                                  XATTN_VT(((ST) + 3) % NSTAGE), cplan, skg, svg,      \
                                  XATTN_KEY0(t + 3), L, wave);                         \
-    else if (t >= chunk_t0 && t - chunk_t0 < n_chunks)                                \
-      token_copy<D, WAVES>(XATTN_KT(((ST) + 3) % NSTAGE), XATTN_VT(((ST) + 3) % NSTAGE), \
-                           cplan, ukg, uvg, kSpareRows + (t - chunk_t0) * KT, n_tok, nb, BW,    \
-                           anc_lds, step, wave);                                      \
+    else if (XATTN_COPIED(t))                                                         \
+      token_chunk_copy_rows<D, WAVES>(XATTN_KT(((ST) + 3) % NSTAGE),                   \
+                                      XATTN_VT(((ST) + 3) % NSTAGE), cplan, ukg, uvg,  \
+                                      chunk_rows[t - chunk_t0 > 0 ? 1 : 0], wave);    \
     _Pragma("unroll") for (int i = 0; i < NKB; ++i) s_cur[i] = s_next[i];             \
   }
   static_assert(NSTAGE == 4, "the tile loop below is unrolled for 4 stages");
@@ -836,6 +951,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     XATTN_TILE_STEP(3)
   }
 #undef XATTN_TILE_STEP
+#undef XATTN_COPIED
   if (n_tiles > 0) {  // the last tile: every copy has landed
     const int t = n_tiles - 1;
     const int lo = t * KT;            // keys below were counted by earlier tiles
@@ -849,34 +965,49 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   }
 #undef XATTN_KEY0
 
-  // ---- Unshared stage from the gathered token rows: the first ones, the
-  // chunks copied in the loop (chunk j in stage (chunk_t0 + j + 3) %
-  // NSTAGE), then any others one at a time through stage 0
+  // ---- Unshared stage from the gathered token blocks, on the matrix
+  // cores: key half kh takes blocks kh, kh + KSPLIT, ... of its row group;
+  // block 0 and the chunks copied in the loop (chunk c in stage
+  // (chunk_t0 + c + 3) % NSTAGE) first, then any other chunks one at a time
+  // through stage 0.
   if constexpr (!TAPS) {
     if (lds_tokens) {
-      const int bi = beam - b_lo;
       const int n_pref = min(n_chunks, max(0, n_tiles - 1 - chunk_t0));
+      const int grow = row0 + rg * 32;
+      const int gfirst = grow / G;
+      const int n_valid = max(0, min((grow + 31) / G, BW - 1) - gfirst + 1) * nlev;
+      // this row's tokens: its beam's nlev levels, within the group's valid tokens
+      const int tok_lo = ((grow + ql) / G - gfirst) * nlev;
+      const int tok_hi = min(tok_lo + nlev, n_valid);
       wait_vm_lgkm0<0>();
-      lds_barrier();  // the tokens are in; every wave is done with the prompt tiles
-      unshared_chunk<D, KSPLIT>(st, qf, XATTN_SK, XATTN_SV, 0, min(n_tok, kSpareRows), nb, bi, kh,
-                                c, lane);
+      lds_barrier();  // the blocks are in; every wave is done with the prompt tiles
+      // ch = -1: block 0 in its region; ch >= 0: chunk ch
 #pragma unroll 1
-      for (int j = 0; j < n_pref; ++j) {
-        const int sg = (chunk_t0 + j + 3) % NSTAGE;
-        const int i0 = kSpareRows + j * KT;
-        unshared_chunk<D, KSPLIT>(st, qf, XATTN_KT(sg), XATTN_VT(sg), i0, min(n_tok, i0 + KT), nb,
-                                  bi, kh, c, lane);
-      }
+      for (int ch = -1; ch < n_chunks; ++ch) {
+        const uint8_t *kt, *vt;
+        if (ch < 0) {
+          kt = XATTN_SK;
+          vt = XATTN_SV;
+        } else if (ch < n_pref) {
+          const int sg = (chunk_t0 + ch + 3) % NSTAGE;
+          kt = tiles + sg * Gm::TILE_BYTES;
+          vt = tiles + (NSTAGE + sg) * Gm::TILE_BYTES;
+        } else {
+          lds_barrier();  // no wave still reads stage 0
+          token_chunk_copy<D, WAVES>(XATTN_KT(0), XATTN_VT(0), cplan, ukg, uvg, tmap, ch, wave);
+          wait_vm_lgkm0<0>();
+          lds_barrier();
+          kt = XATTN_KT(0);
+          vt = XATTN_VT(0);
+        }
 #pragma unroll 1
-      for (int j = n_pref; j < n_chunks; ++j) {
-        const int i0 = kSpareRows + j * KT;
-        lds_barrier();  // no wave still reads stage 0
-        token_copy<D, WAVES>(XATTN_KT(0), XATTN_VT(0), cplan, ukg, uvg, i0, n_tok, nb, BW,
-                             anc_lds, step, wave);
-        wait_vm_lgkm0<0>();
-        lds_barrier();
-        unshared_chunk<D, KSPLIT>(st, qf, XATTN_KT(0), XATTN_VT(0), i0, min(n_tok, i0 + KT), nb,
-                                  bi, kh, c, lane);
+        for (int b = kh; b < n_blk; b += KSPLIT) {
+          const int gb = b * RG + rg;
+          if ((gb == 0) != (ch < 0) || (gb > 0 && ((gb - 1) >> 1) != ch)) continue;
+          const int off = gb == 0 ? 0 : 32 * ((gb - 1) & 1) * Gm::RB;
+          token_block<D, KSPLIT>(st, qf, kt + off, vt + off, fo, kh, 32 * b, tok_lo, tok_hi, c,
+                                 thr, lane);
+        }
       }
     }
   }
