@@ -541,17 +541,28 @@ struct TokenMap {
   // i / nlev == (i * nlev_magic) >> 20 for the token counts used here
   // (i * nlev < 2^20), nlev_magic = floor(2^20 / nlev) + 1
   uint32_t nlev_magic;
-  int first[RG];   // first beam of each row group, from the row block's first beam
-  __device__ void init(const int32_t *anc, int n_blk_, int nlev_, int BW_, int nb_, int G,
-                       int row0, int b_lo) {
+  // first beam of row group g, from the row block's first beam:
+  // (row0 + 32 g) / G - b_lo, which is first0 + g * gstep when G divides 32
+  // (a scalar formula: an array indexed by g would live in scratch memory)
+  int first0, gstep, G, row0, b_lo;
+  bool linear;
+  __device__ void init(const int32_t *anc, int n_blk_, int nlev_, int BW_, int nb_, int G_,
+                       int row0_, int b_lo_) {
     anc_lds = anc;
     n_blk = n_blk_;
     nlev = nlev_;
     BW = BW_;
     nb = nb_;
     nlev_magic = (1u << 20) / (uint32_t)nlev_ + 1u;
-#pragma unroll
-    for (int g = 0; g < RG; ++g) first[g] = (row0 + 32 * g) / G - b_lo;
+    G = G_;
+    row0 = row0_;
+    b_lo = b_lo_;
+    linear = 32 % G_ == 0;
+    first0 = row0_ / G_ - b_lo_;
+    gstep = linear ? 32 / G_ : 0;
+  }
+  __device__ int first(int g) const {
+    return linear ? first0 + g * gstep : (row0 + 32 * g) / G - b_lo;
   }
   // row index (level * BW + slot) of row r of block gb in the (request, KV
   // head) slice of the unshared cache
@@ -561,10 +572,7 @@ struct TokenMap {
     const int i = 32 * b + r;
     const int jb = (int)(((uint32_t)i * nlev_magic) >> 20);
     const int lvl = i - jb * nlev;
-    int f = first[0];
-#pragma unroll
-    for (int k = 1; k < RG; ++k) f = g == k ? first[k] : f;
-    const int bi = clampi(f + jb, 0, nb - 1);
+    const int bi = clampi(first(g) + jb, 0, nb - 1);
     return lvl * BW + anc_lds[bi * nlev + lvl];
   }
   // element offset of row r of block gb in the (request, KV head) slice
@@ -574,10 +582,7 @@ struct TokenMap {
     const int i = 32 * b + r;
     const int jb = (int)(((uint32_t)i * nlev_magic) >> 20);
     const int lvl = i - jb * nlev;
-    int f = first[0];
-#pragma unroll
-    for (int k = 1; k < RG; ++k) f = g == k ? first[k] : f;
-    const int bi = clampi(f + jb, 0, nb - 1);
+    const int bi = clampi(first(g) + jb, 0, nb - 1);
     const int slot = anc_lds[bi * nlev + lvl];
     return ((int64_t)lvl * BW + slot) * D;
   }
@@ -867,15 +872,16 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // rows of the two chunks the loop may copy (the last two steps), read
   // from LDS now, while no copy into LDS is in flight
   constexpr int B0PW = block0_copies_per_wave<D, WAVES>();
-  int chunk_rows[2][CopyPlan<D, WAVES>::PER];
+  // (two named arrays: an array indexed by a runtime chunk number would
+  // live in scratch memory)
+  int chunk_rows0[CopyPlan<D, WAVES>::PER], chunk_rows1[CopyPlan<D, WAVES>::PER];
   if (lds_tokens) {
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-      for (int i = 0; i < CopyPlan<D, WAVES>::PER; ++i) {
-        const int row = CopyPlan<D, WAVES>::row_of(cplan.off[i]);
-        chunk_rows[ch][i] = tmap.row_index(1 + 2 * ch + row / 32, row % 32);
-      }
+    for (int i = 0; i < CopyPlan<D, WAVES>::PER; ++i) {
+      const int row = CopyPlan<D, WAVES>::row_of(cplan.off[i]);
+      chunk_rows0[i] = tmap.row_index(1 + row / 32, row % 32);
+      chunk_rows1[i] = tmap.row_index(3 + row / 32, row % 32);
+    }
     token_block0_copy<D, WAVES>(XATTN_SK, XATTN_SV, ukg, uvg, tmap, wave, lane);
   }
 
@@ -937,10 +943,14 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       tile_copy<D, WAVES, false>(XATTN_KT(((ST) + 3) % NSTAGE),                       \
                                  XATTN_VT(((ST) + 3) % NSTAGE), cplan, skg, svg,      \
                                  XATTN_KEY0(t + 3), L, wave);                         \
-    else if (XATTN_COPIED(t))                                                         \
+    else if (XATTN_COPIED(t)) {                                                       \
+      int rows_t[CopyPlan<D, WAVES>::PER];                                            \
+      _Pragma("unroll") for (int i = 0; i < CopyPlan<D, WAVES>::PER; ++i)             \
+        rows_t[i] = t > chunk_t0 ? chunk_rows1[i] : chunk_rows0[i];                   \
       token_chunk_copy_rows<D, WAVES>(XATTN_KT(((ST) + 3) % NSTAGE),                   \
                                       XATTN_VT(((ST) + 3) % NSTAGE), cplan, ukg, uvg,  \
-                                      chunk_rows[t - chunk_t0 > 0 ? 1 : 0], wave);    \
+                                      rows_t, wave);                                  \
+    }                                                                                 \
     _Pragma("unroll") for (int i = 0; i < NKB; ++i) s_cur[i] = s_next[i];             \
   }
   static_assert(NSTAGE == 4, "the tile loop below is unrolled for 4 stages");
