@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--per-beam-steps", type=int, default=10,
+                    help="steps of the per-beam comparison kernel timed after the main run "
+                         "(0 skips it)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -215,6 +218,32 @@ def main():
     per_call = np.array([[ev[k][2 * i].elapsed_time(ev[k][2 * i + 1]) for i in range(n_calls)]
                          for k in range(args.steps)])
     mean_launch_s = per_call.mean(axis=0) / 1e3
+
+    # the per-beam (PagedAttention-style) comparison kernel on the same inputs,
+    # outside the timed region: its per-launch duration, as the staged one's
+    per_beam = None
+    if args.per_beam_steps > 0:
+        pb_calls = [[B.PreparedDecode(c["q"][i], c["sk"], c["sv"], c["pl"], c["uk"], c["uv"],
+                                      c["par"], w.steps[i], per_beam=True)
+                     for i in range(n_calls)] for c in copies]
+        pb_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
+                 for _ in range(args.per_beam_steps + 1)]
+        for row in pb_ev:
+            for e in row:
+                e.record(stream)
+        for k in range(args.per_beam_steps + 1):   # the first step is a warmup
+            for i, call in enumerate(pb_calls[k % n_rot]):
+                call(stream, (pb_ev[k][2 * i], pb_ev[k][2 * i + 1]))
+        torch.cuda.synchronize()
+        pb = np.array([[pb_ev[k][2 * i].elapsed_time(pb_ev[k][2 * i + 1]) for i in range(n_calls)]
+                       for k in range(1, args.per_beam_steps + 1)])
+        pb_us = float(pb.mean() * 1e3)
+        per_beam = {"kernel_us_per_launch": pb_us,
+                    "staged_speedup": pb_us / (float(per_call.mean()) * 1e3),
+                    "prompt_bytes_read_per_launch": float(
+                        2 * w.elem_bytes * w.D * w.Hkv * w.BW * int(np.sum(w.prompt_len))),
+                    "steps": args.per_beam_steps}
+
     t_kernel = float(mean_launch_s.mean())
     bytes_per_launch = float(np.mean([x["bytes"] for x in work]))
     flops_per_launch = float(np.mean([x["flops"] for x in work]))
@@ -260,6 +289,7 @@ def main():
                                    "flops": flops_per_launch},
         "kernel_sha256_16": kernel_digest(w.dtype),
         "cpu_baseline": None,
+        "per_beam_comparison": per_beam,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

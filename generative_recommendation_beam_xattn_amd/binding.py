@@ -36,7 +36,8 @@ class Shape(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
-EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_workspace_size",
+EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_decode_per_beam",
+           "xattn_decode_per_beam_timed", "xattn_workspace_size",
            "xattn_resolve_ancestors", "xattn_status_string", "xattn_last_error")
 
 
@@ -62,6 +63,10 @@ def load():
         lib.xattn_decode_debug.restype = ctypes.c_int
         lib.xattn_decode_timed.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P, P, P]
         lib.xattn_decode_timed.restype = ctypes.c_int
+        lib.xattn_decode_per_beam.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P]
+        lib.xattn_decode_per_beam.restype = ctypes.c_int
+        lib.xattn_decode_per_beam_timed.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P, P, P]
+        lib.xattn_decode_per_beam_timed.restype = ctypes.c_int
         lib.xattn_workspace_size.argtypes = [S, i32]
         lib.xattn_workspace_size.restype = sz
         lib.xattn_resolve_ancestors.argtypes = [S, P, i32, P, P]
@@ -178,6 +183,22 @@ def decode(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx
     return out
 
 
+def decode_per_beam(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+                    out=None, workspace=None, scale: float = 0.0, stream=None):
+    """The per-beam (PagedAttention-style) comparison kernel; same result as decode."""
+    lib = load()
+    _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
+    shape = make_shape(q, shared_k, unshared_k, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    ws, ws_bytes = _workspace(shape, step, workspace, q.device)
+    _check(lib.xattn_decode_per_beam(ctypes.byref(shape), _ptr(q), _ptr(shared_k), _ptr(shared_v),
+                                     _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v),
+                                     _ptr(parent_idx), int(step), _ptr(out), _ptr(ws), ws_bytes,
+                                     _stream(stream, q.device)))
+    return out
+
+
 def decode_debug(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
                  scale: float = 0.0, stream=None, lse=True, stages=True):
     """Staged decode with explicit merge; returns (out, lse, stage_ml, stage_o).
@@ -225,7 +246,7 @@ class PreparedDecode:
     """
 
     def __init__(self, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx,
-                 step, out=None, workspace=None, scale: float = 0.0):
+                 step, out=None, workspace=None, scale: float = 0.0, per_beam: bool = False):
         _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
         self.lib = load()
         self.shape = make_shape(q, shared_k, unshared_k, scale)
@@ -233,6 +254,9 @@ class PreparedDecode:
         self.ws, ws_bytes = _workspace(self.shape, step, workspace, q.device)
         self._keep = (q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
         self.device = q.device
+        self.fn = self.lib.xattn_decode_per_beam if per_beam else self.lib.xattn_decode
+        self.fn_timed = (self.lib.xattn_decode_per_beam_timed if per_beam
+                         else self.lib.xattn_decode_timed)
         self.args = (ctypes.byref(self.shape), _ptr(q), _ptr(shared_k), _ptr(shared_v),
                      _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v), _ptr(parent_idx),
                      int(step), _ptr(self.out), _ptr(self.ws), ws_bytes)
@@ -242,10 +266,10 @@ class PreparedDecode:
         recorded once (torch creates the HIP event on first record); they are
         bound to the attention kernel's dispatch (xattn_decode_timed)."""
         if events is None:
-            st = self.lib.xattn_decode(*self.args, _stream(stream, self.device))
+            st = self.fn(*self.args, _stream(stream, self.device))
         else:
-            st = self.lib.xattn_decode_timed(*self.args, _stream(stream, self.device),
-                                             _event(events[0]), _event(events[1]))
+            st = self.fn_timed(*self.args, _stream(stream, self.device), _event(events[0]),
+                               _event(events[1]))
         if st != XATTN_OK:
             _check(st)
         return self.out

@@ -63,7 +63,8 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
                  const int32_t *prompt_len, const void *unshared_k, const void *unshared_v,
                  const int32_t *parent_idx, int32_t step, void *out, float *lse,
                  float *stage_ml, float *stage_o, bool taps, void *workspace,
-                 size_t workspace_bytes, void *stream, xattn::LaunchEvents ev = {}) {
+                 size_t workspace_bytes, void *stream, xattn::LaunchEvents ev = {},
+                 bool per_beam = false) {
   xattn_status st = check_shape(s, step);
   if (st != XATTN_OK) return st;
   if (!q || !prompt_len || !unshared_k || !unshared_v || !parent_idx || !out)
@@ -121,7 +122,9 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
     p.anc = anc;
   }
   if (s->dtype == XATTN_F32)
-    e = xattn::launch_decode_f32(p, hs, ev);
+    e = xattn::launch_decode_f32(p, hs, ev);  // per query row already: also the per-beam form
+  else if (per_beam)
+    e = xattn::launch_decode_per_beam_bf16(p, hs, ev);
   else
     e = xattn::launch_decode_bf16(p, taps, hs, ev);
   if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
@@ -164,6 +167,30 @@ xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const v
   ev.stop = static_cast<hipEvent_t>(stop_event);
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
              out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream, ev);
+}
+
+xattn_status xattn_decode_per_beam(const xattn_shape *shape, const void *q, const void *shared_k,
+                                   const void *shared_v, const int32_t *prompt_len,
+                                   const void *unshared_k, const void *unshared_v,
+                                   const int32_t *parent_idx, int32_t step, void *out,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+  return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream, {}, true);
+}
+
+xattn_status xattn_decode_per_beam_timed(const xattn_shape *shape, const void *q,
+                                         const void *shared_k, const void *shared_v,
+                                         const int32_t *prompt_len, const void *unshared_k,
+                                         const void *unshared_v, const int32_t *parent_idx,
+                                         int32_t step, void *out, void *workspace,
+                                         size_t workspace_bytes, void *stream, void *start_event,
+                                         void *stop_event) {
+  if (!start_event || !stop_event) return fail(XATTN_EINVAL, "both timing events are required");
+  xattn::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream, ev, true);
 }
 
 size_t xattn_workspace_size(const xattn_shape *shape, int32_t step) {

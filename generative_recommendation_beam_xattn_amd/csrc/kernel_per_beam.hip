@@ -1,0 +1,192 @@
+// Per-beam decode attention: the comparison baseline the xGR summary
+// measures xAttention against (section 1 and section 4: PagedAttention-style
+// kernels run every beam as a sequence of its own and re-read the shared
+// prompt KV for each beam).
+//
+// Same operation and result as the staged kernels -- softmax attention of
+// each query row over [prompt rows 0..L_r-1 ; the beam's own generated
+// token at levels 0..s] -- computed the way a per-sequence decode kernel
+// does it: one workgroup per (request r, beam b, KV head k) streams that
+// beam's whole sequence, the prompt included, for the G query heads of k.
+// Nothing is shared between the beams of a request, so the prompt's K/V
+// cross the memory hierarchy once per beam.
+//
+// A key row (D bf16) is read by LPK = D / 8 lanes, 16 bytes each, so a
+// wave reads 64 / LPK rows per load instruction, fully coalesced.  Each
+// lane group keeps an online-softmax state per query row for the keys it
+// visits (dot products with v_dot2_f32_bf16, reduced over the group); the
+// states of all groups of the 4 waves are merged through LDS at the end.
+#include <hip/hip_ext.h>
+
+#include "xattn_internal.h"
+
+namespace xattn {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kRowsPerPass = 4;   // query rows a pass keeps state for
+
+__device__ inline float lo_f(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float hi_f(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodeParams p) {
+  constexpr int LPK = D / 8;        // lanes per key row
+  constexpr int KPW = 64 / LPK;     // key rows per wave per load
+  constexpr int NSG = kWaves * KPW; // lane groups in the workgroup
+  __shared__ int32_t anc_s[kMaxInKernelLevels];
+  __shared__ float red_o[NSG][kRowsPerPass][D];
+  __shared__ float red_ml[NSG][kRowsPerPass][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane / LPK, part = lane % LPK;
+  const int sg = wave * KPW + sub;
+  const int k = blockIdx.x % p.Hkv;
+  const int b = (blockIdx.x / p.Hkv) % p.BW;
+  const int r = blockIdx.x / (p.Hkv * p.BW);
+  const int step = p.step, BW = p.BW, G = p.G;
+  const float c = p.scale_log2;
+
+  // the beam's ancestor slot at every level: walked here for short chains,
+  // resolved into the workspace beforehand for deep ones
+  if (p.anc == nullptr) {
+    if (tid == 0) {
+      int a = b;
+      anc_s[step] = a;
+      const int32_t *par = p.parent_idx + (int64_t)r * p.S * BW;
+      for (int t = step; t >= 1; --t) {
+        a = min(max(par[(int64_t)t * BW + a], 0), BW - 1);
+        anc_s[t - 1] = a;
+      }
+    }
+    __syncthreads();
+  }
+  auto anc_of = [&](int t) {
+    return p.anc ? min(max(p.anc[((int64_t)r * (step + 1) + t) * BW + b], 0), BW - 1) : anc_s[t];
+  };
+
+  const int L = min(max(p.prompt_len[r], 0), p.Lmax);
+  const int n_keys = L + step + 1;
+  const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  const uint16_t *svg = static_cast<const uint16_t *>(p.shared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  const uint16_t *qg = static_cast<const uint16_t *>(p.q);
+  uint16_t *og = static_cast<uint16_t *>(p.out);
+
+  for (int h0 = 0; h0 < G; h0 += kRowsPerPass) {
+    const int nr = min(kRowsPerPass, G - h0);
+    // this lane's 8 dims of each query row of the pass
+    uint4 qv[kRowsPerPass];
+#pragma unroll
+    for (int j = 0; j < kRowsPerPass; ++j) {
+      const int hh = k * G + h0 + min(j, nr - 1);
+      qv[j] = *reinterpret_cast<const uint4 *>(qg + (((int64_t)r * BW + b) * p.Hq + hh) * D +
+                                               part * 8);
+    }
+    float m[kRowsPerPass], l[kRowsPerPass], o[kRowsPerPass][8];
+#pragma unroll
+    for (int j = 0; j < kRowsPerPass; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
+    }
+    for (int i = sg; i < n_keys; i += NSG) {
+      const uint16_t *kr, *vr;
+      if (i < L) {
+        kr = skg + (int64_t)i * D;
+        vr = svg + (int64_t)i * D;
+      } else {
+        const int t = i - L;
+        const int64_t e = ((int64_t)t * BW + anc_of(t)) * D;
+        kr = ukg + e;
+        vr = uvg + e;
+      }
+      const uint4 kv = *reinterpret_cast<const uint4 *>(kr + part * 8);
+      const uint4 vv = *reinterpret_cast<const uint4 *>(vr + part * 8);
+      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int j = 0; j < kRowsPerPass; ++j) {
+        const uint32_t qw[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[e]),
+                                              __builtin_bit_cast(bf16x2, kw[e]), s, false);
+#pragma unroll
+        for (int w = LPK / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPK);
+        // online softmax of this lane group's keys (scores in exp2 units)
+        const float mn = fmaxf(m[j], s);
+        const float alpha = __builtin_amdgcn_exp2f((m[j] - mn) * c);   // 0 while m is -inf
+        const float pr = __builtin_amdgcn_exp2f((s - mn) * c);
+        m[j] = mn;
+        l[j] = l[j] * alpha + pr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[j][2 * e] = fmaf(o[j][2 * e], alpha, pr * lo_f(vw[e]));
+          o[j][2 * e + 1] = fmaf(o[j][2 * e + 1], alpha, pr * hi_f(vw[e]));
+        }
+      }
+    }
+    // merge the lane groups' states through LDS
+#pragma unroll
+    for (int j = 0; j < kRowsPerPass; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[sg][j][part * 8 + e] = o[j][e];
+      if (part == 0) {
+        red_ml[sg][j][0] = m[j];
+        red_ml[sg][j][1] = l[j];
+      }
+    }
+    __syncthreads();
+    for (int x = tid; x < nr * D; x += kWaves * 64) {
+      const int j = x / D, d = x % D;
+      float mm = -INFINITY;
+      for (int g = 0; g < NSG; ++g) mm = fmaxf(mm, red_ml[g][j][0]);
+      float lt = 0.f, ot = 0.f;
+      for (int g = 0; g < NSG; ++g) {
+        const float mg = red_ml[g][j][0];
+        if (mg == -INFINITY) continue;   // a group that saw no key
+        const float w = __builtin_amdgcn_exp2f((mg - mm) * c);
+        lt += red_ml[g][j][1] * w;
+        ot += red_o[g][j][d] * w;
+      }
+      const int hh = k * G + h0 + j;
+      og[(((int64_t)r * BW + b) * p.Hq + hh) * D + d] =
+          __builtin_bit_cast(uint16_t, (__bf16)(ot / lt));
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream,
+                                       LaunchEvents ev) {
+  const int64_t grid = (int64_t)p.R * p.BW * p.Hkv;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  auto go = [&](auto kernel) {
+    if (ev.start)
+      hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0u, stream,
+                            ev.start, ev.stop, 0u, p);
+    else
+      hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+  };
+  if (p.D == 64)
+    go(decode_per_beam_kernel<64>);
+  else if (p.D == 128)
+    go(decode_per_beam_kernel<128>);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace xattn

@@ -52,6 +52,8 @@ hipError_t launch_resolve_ancestors(const int32_t *parent_idx, int32_t R, int32_
 hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream,
                               LaunchEvents ev = {});
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev = {});
+hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream,
+                                       LaunchEvents ev = {});
 
 // Number of query rows one bf16 workgroup owns for this shape.
 int bf16_rows_per_block(const DecodeParams &p);

@@ -151,6 +151,31 @@ xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const v
                                 void *workspace, size_t workspace_bytes, void *stream,
                                 void *start_event, void *stop_event);
 
+/*
+ * The same attention computed per beam, as a per-sequence decode kernel
+ * (PagedAttention style) would: every (request, beam, KV head) streams the
+ * beam's whole sequence, prompt included, so the prompt's K/V are read once
+ * per beam instead of once per request.  This is the baseline the xGR
+ * summary compares xAttention against (sections 1 and 4); it is kept to
+ * measure that comparison on this hardware.  Arguments, layouts, workspace
+ * and errors as xattn_decode; out matches xattn_decode's within rounding.
+ * For XATTN_F32 it runs the float32 kernel, which already works per query
+ * row.  The _timed form binds two caller events to the kernel dispatch, as
+ * xattn_decode_timed does.
+ */
+xattn_status xattn_decode_per_beam(const xattn_shape *shape, const void *q, const void *shared_k,
+                                   const void *shared_v, const int32_t *prompt_len,
+                                   const void *unshared_k, const void *unshared_v,
+                                   const int32_t *parent_idx, int32_t step, void *out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+xattn_status xattn_decode_per_beam_timed(const xattn_shape *shape, const void *q,
+                                         const void *shared_k, const void *shared_v,
+                                         const int32_t *prompt_len, const void *unshared_k,
+                                         const void *unshared_v, const int32_t *parent_idx,
+                                         int32_t step, void *out, void *workspace,
+                                         size_t workspace_bytes, void *stream, void *start_event,
+                                         void *stop_event);
+
 /* Static description of a status code. */
 const char *xattn_status_string(xattn_status status);
 

@@ -213,6 +213,37 @@ def test_timed_entry_matches_decode(case):
     assert 0.0 < t < 1000.0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_per_beam_small_shapes(name, dtype):
+    w = W.custom(name=name, seed=zlib.crc32(name.encode()) % 1000 + 101, dtype=dtype,
+                 **SMALL[name])
+    dw = DeviceWorkload(w)
+    for i, s in enumerate(w.steps):
+        say("[per-beam %s/%s] step %d" % (name, dtype, s))
+        out = X.decode_per_beam(*dw.args(i))
+        torch.cuda.synchronize()
+        ref, _ = oracle.attend(*host_args(w, i))
+        err = np.max(np.abs(to_f64(out) - ref))
+        assert err <= TOL[w.dtype], "%s step %d: max abs err %g" % (name, s, err)
+
+
+def test_per_beam_gr_serving_sampled_and_close_to_staged():
+    w = W.make(2)
+    dw = DeviceWorkload(w)
+    for i, s in enumerate(w.steps):
+        say("[per-beam gr_serving] step %d" % s)
+        out = X.decode_per_beam(*dw.args(i))
+        staged = X.decode(*dw.args(i))
+        torch.cuda.synchronize()
+        rows = sample_rows(w, 64, seed=40 + i)
+        ref, _ = oracle.attend(*host_args(w, i), rows=rows)
+        got = to_f64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
+        assert np.max(np.abs(got - ref)) <= TOL["bf16"]
+        # both are within the bar of the exact result, so within twice it of each other
+        assert np.max(np.abs(to_f64(out) - to_f64(staged))) <= 2 * TOL["bf16"]
+
+
 def test_invalid_arguments_raise_before_launch():
     w = W.custom(name="inv", seed=1, R=1, BW=2, Hq=2, Hkv=1, D=128, L=[8], steps=[0], S=2)
     dw = DeviceWorkload(w)
