@@ -171,3 +171,67 @@ def custom(*, name="custom", seed=0, R, L, BW, steps, Hq, Hkv, D, dtype="bf16",
                     steps=list(steps), prompt_len=prompt_len, q=q, shared_k=shared_k,
                     shared_v=shared_v, unshared_k=unshared_k, unshared_v=unshared_v,
                     parent_idx=parent_idx, meta=dict(meta or {}, seed=seed, parents=parents))
+
+
+# --- beam-selection inputs --------------------------------------------------
+#
+# One decode step's candidate pool for beam selection (xGR summary, section
+# 2.2 "xBeam"; pool sizes 128x128 and 512x512 from its section 1): every beam
+# of a request proposes its V best next tokens, sorted by log-probability.
+# Recipe (generator ``numpy.random.default_rng(seed)``, draw order cum,
+# logp, token):
+#   * cum [R][BW]: cumulative beam scores, -3 + N(0, 1) as float32;
+#   * logp [R][BW][V]: per row, V draws of 2 * N(0, 1) as float32, sorted
+#     descending, minus the row maximum and ln(VOCAB) so they look like
+#     log-probabilities (<= -ln VOCAB);
+#   * token [R][BW][V]: per row, V distinct ids from a vocabulary of VOCAB
+#     (a random permutation's first V entries).
+# Variants for edge cases: "ties" rounds cum and logp to multiples of 1/4
+# (many equal scores, across and within rows, in random token order);
+# "identical" gives every beam of a request the same cum, logp and token
+# rows (the first step of a search, when all beams hold the same prefix);
+# ``masked_frac`` sets that fraction of each row's tail to -inf, as an
+# item-validity mask does to tokens that lead to no valid item.
+BEAM_VOCAB = 8192
+BEAM_POOLS = {"gr_serving": dict(R=16, BW=128, V=128), "wide_beam": dict(R=8, BW=512, V=512)}
+
+
+@dataclass
+class BeamPool:
+    cum: np.ndarray      # float32 [R][BW]
+    logp: np.ndarray     # float32 [R][BW][V], rows non-increasing
+    token: np.ndarray    # int32 [R][BW][V]
+
+    @property
+    def shape(self):
+        return self.logp.shape
+
+
+def beam_pool(seed: int, R: int, BW: int, V: int, kind: str = "normal",
+              masked_frac: float = 0.0, vocab: int = BEAM_VOCAB) -> BeamPool:
+    if V > vocab:
+        raise ValueError("V must not exceed the vocabulary")
+    rng = np.random.default_rng(seed)
+    cum = (np.float32(-3.0) + rng.standard_normal((R, BW), dtype=np.float32)).astype(np.float32)
+    x = np.float32(2.0) * rng.standard_normal((R, BW, V), dtype=np.float32)
+    x = -np.sort(-x, axis=-1)
+    logp = (x - x[..., :1] - np.float32(np.log(vocab))).astype(np.float32)
+    token = np.empty((R, BW, V), np.int32)
+    for r in range(R):
+        for b in range(BW):
+            token[r, b] = rng.permutation(vocab)[:V]
+    if kind == "ties":
+        cum = (np.round(cum * 4) / 4).astype(np.float32)
+        logp = (np.round(logp * 4) / 4).astype(np.float32)
+    elif kind == "identical":
+        cum = np.repeat(cum[:, :1], BW, axis=1)
+        logp = np.repeat(logp[:, :1], BW, axis=1)
+        token = np.repeat(token[:, :1], BW, axis=1)
+    elif kind != "normal":
+        raise ValueError(kind)
+    if masked_frac > 0:
+        n = int(round(masked_frac * V))
+        if n:
+            logp[..., V - n:] = -np.inf
+    return BeamPool(cum=np.ascontiguousarray(cum), logp=np.ascontiguousarray(logp),
+                    token=np.ascontiguousarray(token))

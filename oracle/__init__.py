@@ -26,7 +26,7 @@ import threading
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "xattn_oracle.c")
+_SRCS = [os.path.join(_HERE, "xattn_oracle.c"), os.path.join(_HERE, "beam_topk_oracle.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -34,10 +34,12 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile the C oracle into ``oracle/liboracle.so`` with gcc."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    stale = (not os.path.exists(_LIB)
+             or os.path.getmtime(_LIB) < max(os.path.getmtime(s) for s in _SRCS))
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
-                        "-Wall", "-o", tmp, _SRC, "-lm"], check=True)
+                        "-Wall", "-o", tmp] + _SRCS + ["-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -63,6 +65,8 @@ def _load():
             lib.oracle_stage_partials.restype = ctypes.c_int
             lib.oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int32] + [P] * 6
             lib.oracle_merge.restype = None
+            lib.oracle_beam_topk.argtypes = [ctypes.c_int32] * 3 + [P] * 6
+            lib.oracle_beam_topk.restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -184,6 +188,31 @@ def merge(ml_a, o_a, ml_b, o_b):
     lse = np.empty(o_a.shape[:-1], np.float64)
     _load().oracle_merge(n, D, _ptr(ml_a), _ptr(o_a), _ptr(ml_b), _ptr(o_b), _ptr(out), _ptr(lse))
     return out, lse
+
+
+def beam_topk(cum, logp, token):
+    """Beam selection of one decode step (xGR summary, section 2.2 "xBeam").
+
+    cum [R][BW] float32, logp [R][BW][V] float32 (rows sorted descending),
+    token [R][BW][V] int32.  Every candidate (b, j) scores the float32 sum
+    cum[b] + logp[b][j]; the BW best under (score desc, parent asc, token asc)
+    are returned in that order as (score [R][BW] float32, parent [R][BW]
+    int32, token [R][BW] int32).
+    """
+    cum = _c(cum, np.float32)
+    logp = _c(logp, np.float32)
+    token = _c(token, np.int32)
+    R, BW, V = logp.shape
+    if cum.shape != (R, BW) or token.shape != (R, BW, V):
+        raise ValueError("cum must be [R][BW] and token [R][BW][V] for logp [R][BW][V]")
+    score = np.empty((R, BW), np.float32)
+    parent = np.empty((R, BW), np.int32)
+    new_token = np.empty((R, BW), np.int32)
+    rc = _load().oracle_beam_topk(R, BW, V, _ptr(cum), _ptr(logp), _ptr(token), _ptr(score),
+                                  _ptr(parent), _ptr(new_token))
+    if rc != 0:
+        raise ValueError("oracle_beam_topk: empty shape or NaN score")
+    return score, parent, new_token
 
 
 def omp_threads() -> int:
