@@ -1,4 +1,4 @@
-"""ctypes binding of libxattn.so (include/xattn.h).
+"""ctypes binding of libxattn.so (include/xattn.h, include/xbeam.h).
 
 Argument marshalling only: shapes are read off the tensors, pointers and the
 current HIP stream are passed through, and every step of the computation runs
@@ -38,7 +38,8 @@ class Shape(ctypes.Structure):
 
 EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_decode_per_beam",
            "xattn_decode_per_beam_timed", "xattn_workspace_size",
-           "xattn_resolve_ancestors", "xattn_status_string", "xattn_last_error")
+           "xattn_resolve_ancestors", "xattn_beam_topk", "xattn_beam_topk_timed",
+           "xattn_status_string", "xattn_last_error")
 
 
 def library_path() -> str:
@@ -71,6 +72,11 @@ def load():
         lib.xattn_workspace_size.restype = sz
         lib.xattn_resolve_ancestors.argtypes = [S, P, i32, P, P]
         lib.xattn_resolve_ancestors.restype = ctypes.c_int
+        i64 = ctypes.c_int64
+        lib.xattn_beam_topk.argtypes = [P, P, P, i32, i32, i32, P, P, P, i64, P]
+        lib.xattn_beam_topk.restype = ctypes.c_int
+        lib.xattn_beam_topk_timed.argtypes = [P, P, P, i32, i32, i32, P, P, P, i64, P, P, P]
+        lib.xattn_beam_topk_timed.restype = ctypes.c_int
         lib.xattn_status_string.argtypes = [ctypes.c_int]
         lib.xattn_status_string.restype = ctypes.c_char_p
         lib.xattn_last_error.argtypes = []
@@ -235,6 +241,54 @@ def resolve_ancestors(parent_idx, step: int, stream=None):
     _check(lib.xattn_resolve_ancestors(ctypes.byref(shape), _ptr(parent_idx), int(step),
                                        _ptr(anc), _stream(stream, parent_idx.device)))
     return anc
+
+
+def _rows_out(t, R: int, BW: int, dtype, device):
+    """An [R][BW] output whose rows may be strided (e.g. parent_idx[:, t, :])."""
+    if t.dtype != dtype or t.device != device:
+        raise ValueError("beam outputs must be %s on %s" % (dtype, device))
+    if tuple(t.shape) != (R, BW) or t.stride(1) != 1 or (R > 1 and t.stride(0) < BW):
+        raise ValueError("beam outputs must be [R][BW] with unit stride along BW")
+    return ctypes.c_void_p(t.data_ptr()), (t.stride(0) if R > 1 else BW)
+
+
+def beam_topk(cum, logp, token, out=None, stream=None, events=None):
+    """The BW best next beams of every request (include/xbeam.h).
+
+    cum [R][BW] float32, logp [R][BW][V] float32 (rows non-increasing),
+    token [R][BW][V] int32.  Returns (score, parent, token), each [R][BW]:
+    float32, int32, int32, best first.  ``out`` may pass the three outputs;
+    they may be row-strided views (parent_idx[:, t, :] of an [R][S][BW]
+    array), all with one row stride.  ``events``: optional recorded (start,
+    stop) torch.cuda.Event pair bound to the kernel dispatch.
+    """
+    lib = load()
+    if logp.dim() != 3:
+        raise ValueError("logp must be [R][BW][V]")
+    R, BW, V = logp.shape
+    if logp.dtype != torch.float32 or cum.dtype != torch.float32 or token.dtype != torch.int32:
+        raise ValueError("cum and logp must be float32, token int32")
+    if tuple(cum.shape) != (R, BW) or tuple(token.shape) != (R, BW, V):
+        raise ValueError("cum must be [R][BW] and token [R][BW][V]")
+    dev = logp.device
+    if cum.device != dev or token.device != dev:
+        raise ValueError("all tensors must be on one device")
+    if out is None:
+        out = (torch.empty((R, BW), dtype=torch.float32, device=dev),
+               torch.empty((R, BW), dtype=torch.int32, device=dev),
+               torch.empty((R, BW), dtype=torch.int32, device=dev))
+    (ps, ss), (pp, sp), (pt, stt) = (_rows_out(out[0], R, BW, torch.float32, dev),
+                                     _rows_out(out[1], R, BW, torch.int32, dev),
+                                     _rows_out(out[2], R, BW, torch.int32, dev))
+    if not ss == sp == stt:
+        raise ValueError("the three outputs must share one row stride")
+    args = (_ptr(cum), _ptr(logp), _ptr(token), R, BW, V, ps, pp, pt, ss, _stream(stream, dev))
+    if events is None:
+        st = lib.xattn_beam_topk(*args)
+    else:
+        st = lib.xattn_beam_topk_timed(*args, _event(events[0]), _event(events[1]))
+    _check(st)
+    return out
 
 
 class PreparedDecode:

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "../../include/xattn.h"
+#include "../../include/xbeam.h"
 #include "xattn_internal.h"
 
 namespace {
@@ -132,9 +133,53 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   return XATTN_OK;
 }
 
+xattn_status beam_topk(const float *cum, const float *logp, const int32_t *token, int32_t R,
+                       int32_t BW, int32_t V, float *new_score, int32_t *new_parent,
+                       int32_t *new_token, int64_t out_stride, void *stream,
+                       xattn::LaunchEvents ev = {}) {
+  if (R < 1) return fail(XATTN_EINVAL, "R must be >= 1");
+  if (BW < 1 || BW > XBEAM_MAX_BEAMS) return fail(XATTN_EINVAL, "BW must be in [1, 512]");
+  if (V < 1 || V > (1 << 24)) return fail(XATTN_EINVAL, "V must be in [1, 2^24]");
+  if (out_stride < BW) return fail(XATTN_EINVAL, "out_stride must be >= BW");
+  if ((double)R * BW * V > kMaxElems || (double)R * out_stride > kMaxElems)
+    return fail(XATTN_EINVAL, "an array exceeds 2^40 elements");
+  if (!cum || !logp || !token || !new_score || !new_parent || !new_token)
+    return fail(XATTN_EINVAL, "a required pointer is NULL");
+  const void *ptrs[] = {cum, logp, token, new_score, new_parent, new_token};
+  for (const void *v : ptrs)
+    if (!aligned(v, 4)) return fail(XATTN_EINVAL, "arrays must be 4-byte aligned");
+  static_assert(XBEAM_MAX_BEAMS == xattn::kMaxTopkBeams, "beam limit mismatch");
+  hipError_t e = xattn::launch_beam_topk(cum, logp, token, R, BW, V, new_score, new_parent,
+                                         new_token, out_stride, static_cast<hipStream_t>(stream),
+                                         ev);
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+xattn_status xattn_beam_topk(const float *cum, const float *logp, const int32_t *token,
+                             int32_t R, int32_t BW, int32_t V, float *new_score,
+                             int32_t *new_parent, int32_t *new_token, int64_t out_stride,
+                             void *stream) {
+  return beam_topk(cum, logp, token, R, BW, V, new_score, new_parent, new_token, out_stride,
+                   stream);
+}
+
+xattn_status xattn_beam_topk_timed(const float *cum, const float *logp, const int32_t *token,
+                                   int32_t R, int32_t BW, int32_t V, float *new_score,
+                                   int32_t *new_parent, int32_t *new_token, int64_t out_stride,
+                                   void *stream, void *start_event, void *stop_event) {
+  if (!start_event || !stop_event) return fail(XATTN_EINVAL, "both timing events are required");
+  xattn::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  return beam_topk(cum, logp, token, R, BW, V, new_score, new_parent, new_token, out_stride,
+                   stream, ev);
+}
 
 xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *shared_k,
                           const void *shared_v, const int32_t *prompt_len,

@@ -11,6 +11,9 @@ namespace xattn {
 // the workspace first.
 constexpr int kMaxInKernelLevels = 16;
 
+// Largest beam width the beam-selection kernel takes.
+constexpr int kMaxTopkBeams = 512;
+
 // Everything a decode launch needs; passed by value as a kernel argument.
 struct DecodeParams {
   const void *q;
@@ -54,6 +57,13 @@ hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stre
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream,
                                        LaunchEvents ev = {});
+
+// Beam selection: the BW best of BW x V sorted candidates per request.
+hipError_t launch_beam_topk(const float *cum, const float *logp, const int32_t *tok, int32_t R,
+                            int32_t BW, int32_t V, float *score, int32_t *parent, int32_t *token,
+                            int64_t out_stride, hipStream_t stream, LaunchEvents ev = {});
+// Candidates per row the beam-selection kernel samples into LDS.
+int beam_topk_sample_len(int32_t BW, int32_t V);
 
 // Number of query rows one bf16 workgroup owns for this shape.
 int bf16_rows_per_block(const DecodeParams &p);

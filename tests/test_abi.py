@@ -1,6 +1,7 @@
-"""The C-ABI library loads, exports what include/xattn.h declares, and rejects
+"""The C-ABI library loads, exports what include/*.h declare, and rejects
 bad arguments before enqueuing anything (no GPU needed, no compute calls)."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -10,12 +11,14 @@ import pytest
 from generative_recommendation_beam_xattn_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "xattn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\S.*?\b(xattn_\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        names |= set(re.findall(r"^\S.*?\b(xattn_\w+)\s*\(", open(h).read(), flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -34,12 +37,18 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) <= exported
 
 
+def test_headers_found():
+    assert [os.path.basename(h) for h in HEADERS] == ["xattn.h", "xbeam.h"]
+    assert len(declared_functions()) == len(B.EXPORTS)
+
+
 @pytest.mark.parametrize("lang", ["c", "c++"])
-def test_header_is_plain_c_and_cxx(lang, tmp_path):
+@pytest.mark.parametrize("header", ["xattn.h", "xbeam.h"])
+def test_header_is_plain_c_and_cxx(lang, header, tmp_path):
     src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
-    src.write_text('#include "xattn.h"\nint main(void){xattn_shape s; (void)s; return 0;}\n')
+    src.write_text('#include "%s"\nint main(void){xattn_shape s; (void)s; return 0;}\n' % header)
     cc = "gcc" if lang == "c" else "g++"
-    subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+    subprocess.run([cc, "-fsyntax-only", "-Wall", "-Werror", "-I", os.path.dirname(HEADERS[0]),
                     str(src)], check=True)
 
 
@@ -145,3 +154,42 @@ def test_alignment_and_workspace_checks(lib):
     st = lib.xattn_decode(ctypes.byref(shape()), q, None, None, pl, uk, uv, par, 0, out, None, 0,
                           None)
     assert st == 1 and "shared" in lib.xattn_last_error().decode()
+
+
+BAD_TOPK = [
+    (dict(R=0), "R must"),
+    (dict(BW=0), "BW must"),
+    (dict(BW=513), "BW must"),
+    (dict(V=0), "V must"),
+    (dict(V=(1 << 24) + 1), "V must"),
+    (dict(stride=3), "out_stride"),
+    (dict(R=1 << 20, BW=512, V=1 << 20, stride=512), "2^40"),
+]
+
+
+@pytest.mark.parametrize("kw,msg", BAD_TOPK)
+def test_beam_topk_bad_sizes_rejected_before_launch(lib, kw, msg):
+    a = dict(R=2, BW=4, V=8, stride=4)
+    a.update(kw)
+    st = lib.xattn_beam_topk(None, None, None, a["R"], a["BW"], a["V"], None, None, None,
+                             a["stride"], None)
+    assert st == 1 and msg in lib.xattn_last_error().decode()
+
+
+def test_beam_topk_null_and_events_rejected(lib):
+    assert lib.xattn_beam_topk(None, None, None, 2, 4, 8, None, None, None, 4, None) == 1
+    assert "NULL" in lib.xattn_last_error().decode()
+    fake = ctypes.c_void_p(0x1000)
+    for start, stop in ((None, fake), (fake, None)):
+        st = lib.xattn_beam_topk_timed(None, None, None, 2, 4, 8, None, None, None, 4, None,
+                                       start, stop)
+        assert st == 1 and "event" in lib.xattn_last_error().decode()
+
+
+@needs_no_gpu
+def test_beam_topk_alignment_checked(lib):
+    ok = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(6)]
+    bad = list(ok)
+    bad[3] = ctypes.c_void_p(0x40002)
+    st = lib.xattn_beam_topk(*bad[:3], 2, 4, 8, *bad[3:], 4, None)
+    assert st == 1 and "aligned" in lib.xattn_last_error().decode()
