@@ -16,8 +16,12 @@ region (wall clock between two device synchronisations).  `roofline` covers
 the decode kernel: algorithmic bytes (unique KV rows + q + out + indices) or
 FLOPs per launch divided by the kernel's mean launch duration, measured with
 a pair of HIP events bound to each kernel dispatch (xattn_decode_timed), so
-the duration is the kernel's own, as a kernel trace reports it.  `cpu_baseline` times the float64 CPU
-oracle on the host cores on a bounded sample of the same workload.
+the duration is the kernel's own, as a kernel trace reports it.
+`cpu_baseline` times the float64 CPU oracle on the host cores on a bounded
+sample of the same workload.  After the timed region, two side legs time
+other kernels on the same device: `per_beam_comparison` (the per-beam
+PagedAttention-style kernel on the same inputs) and `beam_selection` (the
+top-BW beam selection on the workload's BW x BW candidate pool).
 """
 from __future__ import annotations
 
@@ -56,6 +60,9 @@ def parse():
     ap.add_argument("--per-beam-steps", type=int, default=10,
                     help="steps of the per-beam comparison kernel timed after the main run "
                          "(0 skips it)")
+    ap.add_argument("--topk-steps", type=int, default=50,
+                    help="launches of beam selection (xattn_beam_topk) timed after the main run "
+                         "on the workload's BW x BW candidate pool (0 skips it)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -140,11 +147,65 @@ def cpu_baseline(w, target_s: float) -> dict:
             n_pairs += 1
             if t_total >= target_s:
                 break
+    # beam selection on the workload's BW x BW pool, for the beam_selection leg
+    from generative_recommendation_beam_xattn_amd import workloads as W
+    BW = min(w.BW, 512)
+    pool = W.beam_pool(100 + w.meta.get("config", 0), w.R, BW, BW)
+    reps, t_sel = 0, 0.0
+    while t_sel < 1.0 and reps < 50:
+        t0 = time.perf_counter()
+        oracle.beam_topk(pool.cum, pool.logp, pool.token)
+        t_sel += time.perf_counter() - t0
+        reps += 1
     return {"value": beam_steps / t_total, "unit": "beam-steps/s", "cores": oracle.omp_threads(),
+            "beam_selection_us_per_launch": t_sel / reps * 1e6,
             "kind": "oracle",
             "sample": "%d (request, decode step) pairs of the %s workload (%d per full pass), %d "
                       "beams each, %.1f s of float64 oracle time" % (
                           n_pairs, w.name, len(order), w.BW, t_total)}
+
+
+# ------------------------------------------------------------ beam selection
+
+def beam_selection_leg(w, steps: int, dev) -> dict:
+    """xattn_beam_topk on the workload's candidate pool: every beam proposes
+    BW candidates (the BW x BW pools of the xGR summary), R requests per
+    launch.  Per-launch kernel time from events bound to the dispatch; for
+    scale, torch.topk over the flattened scores of the same pool (a
+    different tie order, so only its time is reported)."""
+    import torch
+    from generative_recommendation_beam_xattn_amd import binding as B
+    from generative_recommendation_beam_xattn_amd import workloads as W
+    BW = min(w.BW, 512)
+    pool = W.beam_pool(100 + w.meta.get("config", 0), w.R, BW, BW)
+    cum = torch.from_numpy(pool.cum).to(dev)
+    logp = torch.from_numpy(pool.logp).to(dev)
+    tok = torch.from_numpy(pool.token).to(dev)
+    out = B.beam_topk(cum, logp, tok)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for pair in ev:
+        for e in pair:
+            e.record()
+    torch.cuda.synchronize()
+    for pair in ev:
+        B.beam_topk(cum, logp, tok, out=out, events=pair)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev]) * 1e3)
+    flat = (cum[:, :, None] + logp).reshape(w.R, -1)
+    for _ in range(3):
+        torch.topk(flat, BW, dim=1)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        torch.topk(flat, BW, dim=1)
+    b.record()
+    torch.cuda.synchronize()
+    n_cand = w.R * BW * BW
+    return {"pool": {"R": w.R, "BW": BW, "V": BW}, "kernel_us_per_launch": us,
+            "candidates_per_s": n_cand / (us * 1e-6), "selections_per_s": w.R * BW / (us * 1e-6),
+            "bound": "latency (one workgroup per request)",
+            "torch_topk_flat_us": float(a.elapsed_time(b) * 1e3 / steps), "steps": steps}
 
 
 # ---------------------------------------------------------------------- main
@@ -244,6 +305,8 @@ def main():
                         2 * w.elem_bytes * w.D * w.Hkv * w.BW * int(np.sum(w.prompt_len))),
                     "steps": args.per_beam_steps}
 
+    beam_sel = beam_selection_leg(w, args.topk_steps, dev) if args.topk_steps > 0 else None
+
     t_kernel = float(mean_launch_s.mean())
     bytes_per_launch = float(np.mean([x["bytes"] for x in work]))
     flops_per_launch = float(np.mean([x["flops"] for x in work]))
@@ -290,6 +353,7 @@ def main():
         "kernel_sha256_16": kernel_digest(w.dtype),
         "cpu_baseline": None,
         "per_beam_comparison": per_beam,
+        "beam_selection": beam_sel,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
