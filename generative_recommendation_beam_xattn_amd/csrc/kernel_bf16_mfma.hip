@@ -33,12 +33,19 @@
 // fragment reads (ds_read_b64_tr_b16, which transposes 4x4 blocks of bf16
 // across lanes) are free of bank conflicts.
 //
-// Unshared stage: each row's s+1 ancestor tokens are gathered from global
-// memory by the lanes that hold that row (VALU dot products in fp32).  Its
-// (max, sum, output) seed the online-softmax state before the shared tiles
-// stream in, so the Merge is the first online-softmax update.  The debug
-// variant (TAPS) instead keeps the two stages apart, writes each stage's
-// (m, l, o) and merges them explicitly at the end.
+// Unshared stage: for chains of up to 16 levels, the generated-token rows
+// of a row block are gathered into LDS in 32-row blocks laid out like the
+// prompt tiles (TokenMap: row group g's tokens, beam-major and level-minor,
+// each row copied from its beam's ancestor slot at its level).  The first
+// block is copied right after the ancestor walk into a region of its own;
+// the others go into ring stages the prompt stream has finished with.  Each
+// block is contracted on the matrix cores like a 32-key prompt tile, with a
+// block-diagonal mask so that a query row only sees its own beam's tokens,
+// and enters the same online-softmax state: the Merge is that state's
+// update.  Deeper chains, resolved into the workspace beforehand, are
+// gathered from global memory by the lanes that hold the row (VALU dot
+// products in fp32).  The debug variant (TAPS) keeps the two stages apart,
+// writes each stage's (m, l, o) and merges them explicitly at the end.
 #include <hip/hip_ext.h>
 
 #include "xattn_internal.h"
