@@ -190,6 +190,31 @@ def merge(ml_a, o_a, ml_b, o_b):
     return out, lse
 
 
+def reorder_unshared(cache, parent, n_levels: int):
+    """In-place reorder of the Unshared cache after beam selection, as a copy.
+
+    xGR summary, section 2.1 ("in-place updates"): instead of following
+    parent chains, the generated-token rows are moved so that slot b holds
+    beam b's own history.  After a step's selection, with parent[r][b] the
+    slot the new beam b descends from, every row (level t < n_levels, slot
+    b) takes the old row (t, parent[r][b]), for every KV head.  cache is
+    [R][Hkv][S][BW][D] (any dtype), parent [R][BW]; returns the new cache.
+    """
+    cache = np.asarray(cache)
+    parent = np.asarray(parent, np.int64)
+    R, Hkv, S, BW, D = cache.shape
+    if parent.shape != (R, BW) or not 0 <= n_levels <= S:
+        raise ValueError("parent must be [R][BW] and 0 <= n_levels <= S")
+    if parent.size and (parent.min() < 0 or parent.max() >= BW):
+        raise ValueError("parent index out of range")
+    out = cache.copy()
+    for r in range(R):
+        for t in range(n_levels):
+            for b in range(BW):
+                out[r, :, t, b, :] = cache[r, :, t, parent[r, b], :]
+    return out
+
+
 def beam_topk(cum, logp, token):
     """Beam selection of one decode step (xGR summary, section 2.2 "xBeam").
 
