@@ -38,7 +38,8 @@ class Shape(ctypes.Structure):
 
 EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_decode_per_beam",
            "xattn_decode_per_beam_timed", "xattn_workspace_size",
-           "xattn_resolve_ancestors", "xattn_beam_topk", "xattn_beam_topk_timed",
+           "xattn_resolve_ancestors", "xattn_reorder_unshared", "xattn_reorder_unshared_timed",
+           "xattn_beam_topk", "xattn_beam_topk_timed",
            "xattn_status_string", "xattn_last_error")
 
 
@@ -73,6 +74,10 @@ def load():
         lib.xattn_resolve_ancestors.argtypes = [S, P, i32, P, P]
         lib.xattn_resolve_ancestors.restype = ctypes.c_int
         i64 = ctypes.c_int64
+        lib.xattn_reorder_unshared.argtypes = [S, P, P, P, i64, i32, P]
+        lib.xattn_reorder_unshared.restype = ctypes.c_int
+        lib.xattn_reorder_unshared_timed.argtypes = [S, P, P, P, i64, i32, P, P, P]
+        lib.xattn_reorder_unshared_timed.restype = ctypes.c_int
         lib.xattn_beam_topk.argtypes = [P, P, P, i32, i32, i32, P, P, P, i64, P]
         lib.xattn_beam_topk.restype = ctypes.c_int
         lib.xattn_beam_topk_timed.argtypes = [P, P, P, i32, i32, i32, P, P, P, i64, P, P, P]
@@ -241,6 +246,36 @@ def resolve_ancestors(parent_idx, step: int, stream=None):
     _check(lib.xattn_resolve_ancestors(ctypes.byref(shape), _ptr(parent_idx), int(step),
                                        _ptr(anc), _stream(stream, parent_idx.device)))
     return anc
+
+
+def reorder_unshared(unshared_k, unshared_v, parent, n_levels: int, stream=None, events=None):
+    """In place: row (t, b) of every request and KV head takes old row
+    (t, parent[r][b]) for t < n_levels (xattn_reorder_unshared).
+
+    unshared_k/v [R][Hkv][S][BW][D] (float32 or bfloat16); parent [R][BW]
+    int32 whose rows may be strided (e.g. parent_idx[:, s, :]).
+    """
+    lib = load()
+    if unshared_k.dim() != 5 or unshared_v.shape != unshared_k.shape:
+        raise ValueError("unshared_k/v must be [R][Hkv][S][BW][D] of one shape")
+    if unshared_v.dtype != unshared_k.dtype or unshared_v.device != unshared_k.device:
+        raise ValueError("unshared_k/v must share dtype and device")
+    R, Hkv, S, BW, D = unshared_k.shape
+    if parent.dtype != torch.int32 or tuple(parent.shape) != (R, BW) or parent.stride(1) != 1:
+        raise ValueError("parent must be int32 [R][BW] with unit stride along BW")
+    if parent.device != unshared_k.device:
+        raise ValueError("all tensors must be on one device")
+    shape = Shape(R, BW, Hkv, Hkv, D, 0, S, _dtype_code(unshared_k), 0.0)
+    stride = parent.stride(0) if R > 1 else BW
+    args = (ctypes.byref(shape), _ptr(unshared_k), _ptr(unshared_v),
+            ctypes.c_void_p(parent.data_ptr()), stride, int(n_levels),
+            _stream(stream, unshared_k.device))
+    if events is None:
+        st = lib.xattn_reorder_unshared(*args)
+    else:
+        st = lib.xattn_reorder_unshared_timed(*args, _event(events[0]), _event(events[1]))
+    _check(st)
+    return unshared_k, unshared_v
 
 
 def _rows_out(t, R: int, BW: int, dtype, device):

@@ -157,9 +157,61 @@ xattn_status beam_topk(const float *cum, const float *logp, const int32_t *token
   return XATTN_OK;
 }
 
+xattn_status reorder_unshared(const xattn_shape *s, void *unshared_k, void *unshared_v,
+                              const int32_t *parent, int64_t parent_stride, int32_t n_levels,
+                              void *stream, xattn::LaunchEvents ev = {}) {
+  xattn_status st = check_shape(s, 0);
+  if (st != XATTN_OK) return st;
+  if (n_levels < 0 || n_levels > s->max_steps)
+    return fail(XATTN_EINVAL, "n_levels must be in [0, max_steps]");
+  if (!unshared_k || !unshared_v || !parent) return fail(XATTN_EINVAL, "a required pointer is NULL");
+  if (!aligned(unshared_k, 16) || !aligned(unshared_v, 16))
+    return fail(XATTN_EINVAL, "unshared_k/unshared_v must be 16-byte aligned");
+  if (!aligned(parent, 4)) return fail(XATTN_EINVAL, "int32 arrays must be 4-byte aligned");
+  if (parent_stride < s->beam_width) return fail(XATTN_EINVAL, "parent_stride must be >= beam_width");
+  if ((double)s->num_requests * parent_stride > kMaxElems)
+    return fail(XATTN_EINVAL, "parent rows exceed 2^40 elements");
+  if (s->beam_width > xattn::kMaxReorderBeams)
+    return fail(XATTN_EUNSUPPORTED, "beam_width above 2048 is not supported by the reorder");
+  xattn::ReorderParams p{};
+  p.unshared_k = unshared_k;
+  p.unshared_v = unshared_v;
+  p.parent = parent;
+  p.parent_stride = parent_stride;
+  p.row_bytes = (int64_t)s->head_dim * (s->dtype == XATTN_F32 ? 4 : 2);
+  p.chunk_bytes = xattn::reorder_chunk_bytes(p.row_bytes, s->beam_width);
+  p.R = s->num_requests;
+  p.Hkv = s->num_kv_heads;
+  p.S = s->max_steps;
+  p.BW = s->beam_width;
+  p.n_levels = n_levels;
+  hipError_t e = xattn::launch_reorder_unshared(p, static_cast<hipStream_t>(stream), ev);
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+xattn_status xattn_reorder_unshared(const xattn_shape *shape, void *unshared_k, void *unshared_v,
+                                    const int32_t *parent, int64_t parent_stride,
+                                    int32_t n_levels, void *stream) {
+  return reorder_unshared(shape, unshared_k, unshared_v, parent, parent_stride, n_levels, stream);
+}
+
+xattn_status xattn_reorder_unshared_timed(const xattn_shape *shape, void *unshared_k,
+                                          void *unshared_v, const int32_t *parent,
+                                          int64_t parent_stride, int32_t n_levels, void *stream,
+                                          void *start_event, void *stop_event) {
+  if (!start_event || !stop_event) return fail(XATTN_EINVAL, "both timing events are required");
+  xattn::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  return reorder_unshared(shape, unshared_k, unshared_v, parent, parent_stride, n_levels, stream,
+                          ev);
+}
 
 xattn_status xattn_beam_topk(const float *cum, const float *logp, const int32_t *token,
                              int32_t R, int32_t BW, int32_t V, float *new_score,

@@ -13,6 +13,8 @@ constexpr int kMaxInKernelLevels = 16;
 
 // Largest beam width the beam-selection kernel takes.
 constexpr int kMaxTopkBeams = 512;
+// Largest beam width the Unshared-cache reorder takes.
+constexpr int kMaxReorderBeams = 2048;
 
 // Everything a decode launch needs; passed by value as a kernel argument.
 struct DecodeParams {
@@ -57,6 +59,21 @@ hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stre
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream,
                                        LaunchEvents ev = {});
+
+// In-place reorder of the Unshared cache: row (t, b) := old row (t, parent[b])
+// for t < n_levels, every request and KV head.
+struct ReorderParams {
+  void *unshared_k;
+  void *unshared_v;
+  const int32_t *parent;   // [R] rows of BW, stride parent_stride
+  int64_t parent_stride;
+  int64_t row_bytes;       // D * element size
+  int64_t chunk_bytes;     // columns staged per pass (divides row_bytes)
+  int32_t R, Hkv, S, BW, n_levels;
+};
+hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream,
+                                   LaunchEvents ev = {});
+int64_t reorder_chunk_bytes(int64_t row_bytes, int32_t BW);
 
 // Beam selection: the BW best of BW x V sorted candidates per request.
 hipError_t launch_beam_topk(const float *cum, const float *logp, const int32_t *tok, int32_t R,

@@ -176,6 +176,41 @@ xattn_status xattn_decode_per_beam_timed(const xattn_shape *shape, const void *q
                                          size_t workspace_bytes, void *stream, void *start_event,
                                          void *stop_event);
 
+/*
+ * In-place reorder of the Unshared cache after beam selection (xGR summary,
+ * section 2.1: generated-token blocks are updated in place, with direct
+ * indices, free of write-before-read hazards).  The alternative to following
+ * parent chains: afterwards slot b holds beam b's own history, and the next
+ * step's attention can use identity parents.
+ *
+ *   unshared_k/v [R][Hkv][S][BW][D]   updated in place: for every request r,
+ *                                     KV head, level t < n_levels and slot b,
+ *                                     row (t, b) takes the old row
+ *                                     (t, parent[r * parent_stride + b])
+ *   parent       [R] rows of BW int32, row stride parent_stride >= BW; pass
+ *                parent_idx + s * BW with stride S * BW to use row s of a
+ *                parent_idx [R][S][BW] array.  Values outside [0, BW) are
+ *                clamped (a precondition, as for parent_idx).
+ *   n_levels     0 <= n_levels <= S; levels >= n_levels are not touched
+ *
+ * Typical use after the selection that yields the parents of level s+1:
+ * reorder levels 0..s with them, then write level s+1 of every slot.  Every
+ * slice (request, KV head, level) is staged whole before any of its rows is
+ * written, so the result is as if all rows were read before any was
+ * written.  shape supplies R, BW, Hkv, D, S and dtype (head counts and
+ * max_prompt_len must be valid but are otherwise unused); beam_width up to
+ * 2048 (XATTN_EUNSUPPORTED above).  Calls on one cache must not overlap
+ * each other or an attention call reading it.  The _timed form binds two
+ * caller events to the kernel dispatch, as xattn_decode_timed does.
+ */
+xattn_status xattn_reorder_unshared(const xattn_shape *shape, void *unshared_k, void *unshared_v,
+                                    const int32_t *parent, int64_t parent_stride,
+                                    int32_t n_levels, void *stream);
+xattn_status xattn_reorder_unshared_timed(const xattn_shape *shape, void *unshared_k,
+                                          void *unshared_v, const int32_t *parent,
+                                          int64_t parent_stride, int32_t n_levels, void *stream,
+                                          void *start_event, void *stop_event);
+
 /* Static description of a status code. */
 const char *xattn_status_string(xattn_status status);
 

@@ -193,3 +193,24 @@ def test_beam_topk_alignment_checked(lib):
     bad[3] = ctypes.c_void_p(0x40002)
     st = lib.xattn_beam_topk(*bad[:3], 2, 4, 8, *bad[3:], 4, None)
     assert st == 1 and "aligned" in lib.xattn_last_error().decode()
+
+
+def test_reorder_bad_arguments_rejected(lib):
+    s = shape()
+    fake = ctypes.c_void_p(0x10000)
+    # n_levels outside [0, S]
+    for n in (-1, 4):
+        assert lib.xattn_reorder_unshared(ctypes.byref(s), fake, fake, fake, 4, n, None) == 1
+        assert "n_levels" in lib.xattn_last_error().decode()
+    assert lib.xattn_reorder_unshared(ctypes.byref(s), None, fake, fake, 4, 1, None) == 1
+    assert "NULL" in lib.xattn_last_error().decode()
+    assert lib.xattn_reorder_unshared(ctypes.byref(s), fake, fake, fake, 3, 1, None) == 1
+    assert "parent_stride" in lib.xattn_last_error().decode()
+    big = shape(beam_width=4096)
+    assert lib.xattn_reorder_unshared(ctypes.byref(big), fake, fake, fake, 4096, 1, None) == 2
+    assert lib.xattn_reorder_unshared(ctypes.byref(shape(num_requests=0)), fake, fake, fake, 4, 1,
+                                      None) == 1
+    for start, stop in ((None, fake), (fake, None)):
+        st = lib.xattn_reorder_unshared_timed(ctypes.byref(s), fake, fake, fake, 4, 1, None,
+                                              start, stop)
+        assert st == 1 and "event" in lib.xattn_last_error().decode()

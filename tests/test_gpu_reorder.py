@@ -1,0 +1,103 @@
+"""GPU parity of the in-place Unshared-cache reorder (xattn_reorder_unshared).
+
+A pure data movement, so the bar is bit-exactness against the oracle's
+definition.  Beyond that, attention over the reordered cache with identity
+parents must equal attention over the original cache with parent chains, bit
+for bit (the same kernel reads the same rows), and both stay within the
+oracle's tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import generative_recommendation_beam_xattn_amd as X
+from generative_recommendation_beam_xattn_amd import workloads as W
+from tests.gpu_util import TOL, DeviceWorkload, host_args, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def same_bits(a: torch.Tensor, b: np.ndarray) -> bool:
+    a = a.cpu()
+    if a.dtype == torch.bfloat16:
+        return np.array_equal(a.view(torch.int16).numpy().view(np.uint16), b)
+    return np.array_equal(a.numpy().view(np.uint32), np.ascontiguousarray(b).view(np.uint32))
+
+
+CASES = [  # R, Hkv, S, BW, D, dtype, n_levels
+    (2, 2, 4, 8, 64, "f32", 3), (3, 1, 3, 5, 128, "bf16", 3), (1, 4, 6, 128, 128, "bf16", 5),
+    (2, 8, 3, 512, 128, "bf16", 2), (1, 2, 2, 512, 128, "f32", 2), (1, 1, 2, 1000, 64, "bf16", 2),
+    (1, 2, 3, 2048, 64, "f32", 1), (2, 2, 5, 7, 64, "bf16", 0), (2, 2, 5, 7, 64, "bf16", 5)]
+
+
+@pytest.mark.parametrize("R,Hkv,S,BW,D,dtype,n_levels", CASES)
+def test_reorder_matches_oracle(R, Hkv, S, BW, D, dtype, n_levels):
+    say("[reorder] R=%d Hkv=%d S=%d BW=%d D=%d %s n_levels=%d" % (R, Hkv, S, BW, D, dtype,
+                                                                   n_levels))
+    rng = np.random.default_rng(R * 1000 + BW + D)
+    uk = W.normal(rng, (R, Hkv, S, BW, D), dtype)
+    uv = W.normal(rng, (R, Hkv, S, BW, D), dtype)
+    hist = rng.integers(0, BW, size=(R, S + 1, BW), dtype=np.int32)   # parent rows, strided use
+    parent = hist[:, 1, :]
+    dk, dv, dh = to_dev(uk), to_dev(uv), to_dev(hist)
+    X.reorder_unshared(dk, dv, dh[:, 1, :], n_levels)
+    torch.cuda.synchronize()
+    assert same_bits(dk, oracle.reorder_unshared(uk, parent, n_levels))
+    assert same_bits(dv, oracle.reorder_unshared(uv, parent, n_levels))
+
+
+def test_identity_parents_leave_the_cache_alone():
+    rng = np.random.default_rng(5)
+    uk = W.normal(rng, (2, 2, 3, 64, 128), "bf16")
+    dk, dv = to_dev(uk), to_dev(uk.copy())
+    ident = torch.arange(64, dtype=torch.int32, device="cuda").repeat(2, 1)
+    X.reorder_unshared(dk, dv, ident, 3)
+    torch.cuda.synchronize()
+    assert same_bits(dk, uk) and same_bits(dv, uk)
+
+
+def run_reordered(w, dw, step):
+    """Attention at `step` after reordering level by level, identity parents."""
+    uk, uv = dw.unshared_k.clone(), dw.unshared_v.clone()
+    for s in range(1, step + 1):
+        X.reorder_unshared(uk, uv, dw.parent_idx[:, s, :], s)
+    ident = torch.arange(w.BW, dtype=torch.int32, device="cuda").repeat(w.R, w.S, 1).contiguous()
+    i = w.steps.index(step)
+    out = X.decode(dw.q[i], dw.shared_k, dw.shared_v, dw.prompt_len, uk, uv, ident, step)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype,BW,step,S", [("bf16", 24, 2, 3), ("f32", 8, 3, 4),
+                                             ("bf16", 128, 2, 3), ("bf16", 16, 20, 21)])
+def test_attention_after_reorder_equals_chains(dtype, BW, step, S):
+    say("[reorder attention] %s BW=%d step=%d" % (dtype, BW, step))
+    w = W.custom(name="reorder", seed=7 + BW, R=2, L=[200, 67], BW=BW, steps=[step], Hq=8,
+                 Hkv=2, D=128 if dtype == "bf16" else 64, dtype=dtype, S=S)
+    dw = DeviceWorkload(w)
+    chains = X.decode(*dw.args(0))
+    torch.cuda.synchronize()
+    moved = run_reordered(w, dw, step)
+    a, b = chains.cpu(), moved.cpu()
+    if a.dtype == torch.bfloat16:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    assert torch.equal(a, b)
+    ref, _ = oracle.attend(*host_args(w, 0))
+    assert np.max(np.abs(to_f64(moved) - ref)) <= TOL[dtype]
+
+
+def test_gr_serving_pipeline_sampled():
+    # the serving workload's full size: reorder at every level, compare with
+    # the chain result of the same kernel
+    w = W.make(2)
+    dw = DeviceWorkload(w)
+    step = w.steps[-1]
+    chains = X.decode(*dw.args(len(w.steps) - 1))
+    torch.cuda.synchronize()
+    moved = run_reordered(w, dw, step)
+    assert torch.equal(chains.cpu().view(torch.int16), moved.cpu().view(torch.int16))
