@@ -20,8 +20,9 @@ the duration is the kernel's own, as a kernel trace reports it.
 `cpu_baseline` times the float64 CPU oracle on the host cores on a bounded
 sample of the same workload.  After the timed region, two side legs time
 other kernels on the same device: `per_beam_comparison` (the per-beam
-PagedAttention-style kernel on the same inputs) and `beam_selection` (the
-top-BW beam selection on the workload's BW x BW candidate pool).
+PagedAttention-style kernel on the same inputs), `beam_selection` (the
+top-BW beam selection on the workload's BW x BW candidate pool) and
+`unshared_reorder` (the in-place Unshared-cache reorder at each level).
 """
 from __future__ import annotations
 
@@ -63,6 +64,9 @@ def parse():
     ap.add_argument("--topk-steps", type=int, default=50,
                     help="launches of beam selection (xattn_beam_topk) timed after the main run "
                          "on the workload's BW x BW candidate pool (0 skips it)")
+    ap.add_argument("--reorder-steps", type=int, default=20,
+                    help="rounds of the in-place Unshared reorder timed after the main run, on "
+                         "the rotation copies (0 skips it)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -163,6 +167,47 @@ def cpu_baseline(w, target_s: float) -> dict:
             "sample": "%d (request, decode step) pairs of the %s workload (%d per full pass), %d "
                       "beams each, %.1f s of float64 oracle time" % (
                           n_pairs, w.name, len(order), w.BW, t_total)}
+
+
+# ------------------------------------------------------- Unshared-cache reorder
+
+def reorder_leg(w, copies, steps: int, stream) -> dict | None:
+    """xattn_reorder_unshared as a caller would run it after each selection:
+    at every decode level s >= 1 of the workload, levels 0..s-1 take the
+    rows of parent_idx[:, s, :].  Timed per launch with events bound to the
+    dispatch, on the rotation copies (so rows come from HBM).  Algorithmic
+    bytes: every row of a slice read once and every moved row written once,
+    K and V; a slice with identity parents moves nothing."""
+    import torch
+    from generative_recommendation_beam_xattn_amd import binding as B
+    levels = [s for s in w.steps if s >= 1]
+    if not levels or w.BW > 2048:
+        return None
+    n_rot = len(copies)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in levels] for _ in range(steps + 1)]
+    for row in ev:
+        for a, b in row:
+            a.record(stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    for k in range(steps + 1):      # round 0 is a warmup
+        c = copies[k % n_rot]
+        for i, s in enumerate(levels):
+            B.reorder_unshared(c["uk"], c["uv"], c["par"][:, s, :], s, stream=stream,
+                               events=ev[k][i])
+    torch.cuda.synchronize()
+    us = np.array([[a.elapsed_time(b) * 1e3 for a, b in ev[k]] for k in range(1, steps + 1)])
+    row = w.D * w.elem_bytes
+    by_level = []
+    for i, s in enumerate(levels):
+        moved = int(np.sum(w.parent_idx[:, s, :] != np.arange(w.BW)[None, :]))
+        moving_req = int(np.sum(np.any(w.parent_idx[:, s, :] != np.arange(w.BW)[None, :], axis=1)))
+        byts = 2 * w.Hkv * s * row * (moving_req * w.BW + moved)
+        t = float(us[:, i].mean())
+        by_level.append({"level": s, "levels_moved": s, "kernel_us": t, "bytes": byts,
+                         "GBps": byts / t / 1e3, "frac_of_hbm_peak": byts / t / 1e3 / HBM_PEAK_GBS})
+    return {"by_level": by_level, "bound": "hbm", "steps": steps}
 
 
 # ------------------------------------------------------------ beam selection
@@ -306,6 +351,7 @@ def main():
                     "steps": args.per_beam_steps}
 
     beam_sel = beam_selection_leg(w, args.topk_steps, dev) if args.topk_steps > 0 else None
+    reorder = reorder_leg(w, copies, args.reorder_steps, stream) if args.reorder_steps > 0 else None
 
     t_kernel = float(mean_launch_s.mean())
     bytes_per_launch = float(np.mean([x["bytes"] for x in work]))
@@ -354,6 +400,7 @@ def main():
         "cpu_baseline": None,
         "per_beam_comparison": per_beam,
         "beam_selection": beam_sel,
+        "unshared_reorder": reorder,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

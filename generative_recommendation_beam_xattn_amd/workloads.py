@@ -235,3 +235,25 @@ def beam_pool(seed: int, R: int, BW: int, V: int, kind: str = "normal",
             logp[..., V - n:] = -np.inf
     return BeamPool(cum=np.ascontiguousarray(cum), logp=np.ascontiguousarray(logp),
                     token=np.ascontiguousarray(token))
+
+
+# --- valid-item vocabularies ------------------------------------------------
+#
+# Items are fixed-length token paths (xGR summary, section 1: items are
+# identified by token sequences, most sequences map to no item; section 2.2:
+# a pre-built vocabulary of valid items drives the masks).  Recipe (generator
+# ``numpy.random.default_rng(seed)``): the first token of an item follows a
+# Zipf-like law over the vocabulary (rank r drawn with weight 1 / (r + 1),
+# ranks mapped to ids by a random permutation), every later token is uniform
+# over the vocabulary; duplicate items are kept (a vocabulary may list an
+# item twice).  The full-size vocabulary is 2^20 items of 3 tokens over 8192
+# ids, matching the 3 decode steps of the serving workload.
+VALID_ITEMS_FULL = dict(n_items=1 << 20, levels=3, vocab=8192)
+
+
+def valid_items(seed: int, n_items: int, levels: int, vocab: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    w = 1.0 / np.arange(1, vocab + 1)
+    first = rng.permutation(vocab)[rng.choice(vocab, size=n_items, p=w / w.sum())]
+    rest = rng.integers(0, vocab, size=(n_items, levels - 1))
+    return np.concatenate([first[:, None], rest], axis=1).astype(np.int32)

@@ -215,6 +215,35 @@ def reorder_unshared(cache, parent, n_levels: int):
     return out
 
 
+def valid_next_tokens(items, prefix) -> np.ndarray:
+    """Tokens that may follow `prefix` on a valid path (xGR summary, section
+    2.2: xBeam's valid-path constraint, masks generated from a pre-built
+    vocabulary of valid items).  Brute force over the item list: token j is
+    valid after prefix p (length d) iff some item starts with p and has j at
+    position d.  items [N][L] int; prefix a sequence of d < L tokens, or
+    None for a dead beam (no valid continuation).  Returns sorted tokens."""
+    items = np.asarray(items)
+    if prefix is None:
+        return np.zeros(0, np.int64)
+    d = len(prefix)
+    if not 0 <= d < items.shape[1]:
+        raise ValueError("prefix length must be in [0, L)")
+    hit = np.all(items[:, :d] == np.asarray(prefix, items.dtype)[None, :], axis=1)
+    return np.unique(items[hit, d]).astype(np.int64)
+
+
+def apply_valid_mask(items, prefixes, logits):
+    """Masked logits: every token that is not a valid continuation of its
+    beam's prefix becomes -inf, the others keep their value.  prefixes is a
+    list (one per row of logits [n][V]) of token sequences or None."""
+    logits = np.asarray(logits, np.float32)
+    out = np.full_like(logits, -np.inf)
+    for i, p in enumerate(prefixes):
+        ok = valid_next_tokens(items, p)
+        out[i, ok] = logits[i, ok]
+    return out
+
+
 def beam_topk(cum, logp, token):
     """Beam selection of one decode step (xGR summary, section 2.2 "xBeam").
 
