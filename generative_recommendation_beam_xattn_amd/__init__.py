@@ -8,7 +8,7 @@ if it is missing: there is no fallback implementation.
 from . import workloads  # noqa: F401  (seeded inputs; no attention arithmetic)
 
 _BINDING = ("decode", "decode_per_beam", "decode_debug", "resolve_ancestors", "workspace_size",
-            "beam_topk", "reorder_unshared", "library_path",
+            "beam_topk", "reorder_unshared", "trie_build", "ValidPaths", "library_path",
             "XattnError", "PreparedDecode", "load")
 __all__ = list(_BINDING[:-1]) + ["workloads"]
 

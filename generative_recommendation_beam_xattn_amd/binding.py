@@ -28,6 +28,20 @@ class XattnError(RuntimeError):
         self.status = status
 
 
+TRIE_MAX_LEVELS = 8
+
+
+class Trie(ctypes.Structure):
+    """xattn_trie (include/xbeam.h): layout of the valid-path tables."""
+    _fields_ = [("vocab", ctypes.c_int32), ("levels", ctypes.c_int32),
+                ("dense_levels", ctypes.c_int32), ("words", ctypes.c_int32),
+                ("nodes", ctypes.c_int32 * (TRIE_MAX_LEVELS + 1)),
+                ("row_ptr_off", ctypes.c_int64 * TRIE_MAX_LEVELS),
+                ("child_tok_off", ctypes.c_int64 * TRIE_MAX_LEVELS),
+                ("mask_off", ctypes.c_int64 * TRIE_MAX_LEVELS),
+                ("total_bytes", ctypes.c_int64)]
+
+
 class Shape(ctypes.Structure):
     _fields_ = [("num_requests", ctypes.c_int32), ("beam_width", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
@@ -39,7 +53,8 @@ class Shape(ctypes.Structure):
 EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_decode_per_beam",
            "xattn_decode_per_beam_timed", "xattn_workspace_size",
            "xattn_resolve_ancestors", "xattn_reorder_unshared", "xattn_reorder_unshared_timed",
-           "xattn_beam_topk", "xattn_beam_topk_timed",
+           "xattn_beam_topk", "xattn_beam_topk_timed", "xattn_trie_build", "xattn_valid_mask",
+           "xattn_valid_mask_timed", "xattn_trie_advance",
            "xattn_status_string", "xattn_last_error")
 
 
@@ -82,6 +97,15 @@ def load():
         lib.xattn_beam_topk.restype = ctypes.c_int
         lib.xattn_beam_topk_timed.argtypes = [P, P, P, i32, i32, i32, P, P, P, i64, P, P, P]
         lib.xattn_beam_topk_timed.restype = ctypes.c_int
+        T = ctypes.POINTER(Trie)
+        lib.xattn_trie_build.argtypes = [P, i64, i32, i32, i32, T, P, sz]
+        lib.xattn_trie_build.restype = ctypes.c_int
+        lib.xattn_valid_mask.argtypes = [T, P, i32, P, P, i32, i32, i64, P]
+        lib.xattn_valid_mask.restype = ctypes.c_int
+        lib.xattn_valid_mask_timed.argtypes = [T, P, i32, P, P, i32, i32, i64, P, P, P]
+        lib.xattn_valid_mask_timed.restype = ctypes.c_int
+        lib.xattn_trie_advance.argtypes = [T, P, i32, P, P, i64, P, i64, P, i32, i32, P]
+        lib.xattn_trie_advance.restype = ctypes.c_int
         lib.xattn_status_string.argtypes = [ctypes.c_int]
         lib.xattn_status_string.restype = ctypes.c_char_p
         lib.xattn_last_error.argtypes = []
@@ -276,6 +300,80 @@ def reorder_unshared(unshared_k, unshared_v, parent, n_levels: int, stream=None,
         st = lib.xattn_reorder_unshared_timed(*args, _event(events[0]), _event(events[1]))
     _check(st)
     return unshared_k, unshared_v
+
+
+def trie_build(items, vocab: int, dense_levels: int):
+    """Host: valid-path tables from items [N][L] (numpy int32).  Returns
+    (layout, table) with table a numpy uint8 buffer to copy to the device."""
+    import numpy as np
+    lib = load()
+    items = np.ascontiguousarray(items, dtype=np.int32)
+    if items.ndim != 2:
+        raise ValueError("items must be [N][L]")
+    n, L = items.shape
+    lay = Trie()
+    ptr = items.ctypes.data_as(ctypes.c_void_p) if n else None
+    _check(lib.xattn_trie_build(ptr, n, L, int(vocab), int(dense_levels), ctypes.byref(lay),
+                                None, 0))
+    table = np.zeros(int(lay.total_bytes), np.uint8)
+    _check(lib.xattn_trie_build(ptr, n, L, int(vocab), int(dense_levels), ctypes.byref(lay),
+                                table.ctypes.data_as(ctypes.c_void_p), table.nbytes))
+    return lay, table
+
+
+class ValidPaths:
+    """Valid-path tables on one device (built on the host, copied once)."""
+
+    def __init__(self, items, vocab: int, dense_levels: int, device="cuda"):
+        self.layout, host = trie_build(items, vocab, dense_levels)
+        self.table = torch.from_numpy(host).to(device)
+        if self.table.data_ptr() % 256:
+            raise RuntimeError("device table is not 256-byte aligned")
+        self.device = self.table.device
+
+    def root(self, R: int, BW: int):
+        """Node ids of R x BW beams that have generated nothing yet."""
+        return torch.zeros((R, BW), dtype=torch.int32, device=self.device)
+
+    def mask(self, depth: int, node, logits, stream=None, events=None):
+        """In place: logits [R][BW][V] (rows may be strided by a multiple of
+        4) keep only tokens that extend each beam's node; others -> -inf."""
+        lib = load()
+        R, BW = node.shape
+        if node.dtype != torch.int32 or not node.is_contiguous():
+            raise ValueError("node must be contiguous int32 [R][BW]")
+        if logits.dtype != torch.float32 or logits.dim() != 3 or tuple(logits.shape[:2]) != (R, BW):
+            raise ValueError("logits must be float32 [R][BW][V]")
+        if logits.shape[2] != self.layout.vocab or logits.stride(2) != 1 or \
+                logits.stride(0) != BW * logits.stride(1):
+            raise ValueError("logits rows must hold the vocabulary with one row stride")
+        args = (ctypes.byref(self.layout), ctypes.c_void_p(self.table.data_ptr()), int(depth),
+                _ptr(node), ctypes.c_void_p(logits.data_ptr()), R, BW, logits.stride(1),
+                _stream(stream, self.device))
+        if events is None:
+            st = lib.xattn_valid_mask(*args)
+        else:
+            st = lib.xattn_valid_mask_timed(*args, _event(events[0]), _event(events[1]))
+        _check(st)
+        return logits
+
+    def advance(self, depth: int, node, parent, token, out=None, stream=None):
+        """New node ids [R][BW]: the child of node[r][parent] through token."""
+        lib = load()
+        R, BW = node.shape
+        for t in (parent, token):
+            if t.dtype != torch.int32 or tuple(t.shape) != (R, BW) or t.stride(1) != 1:
+                raise ValueError("parent and token must be int32 [R][BW], unit stride along BW")
+        if out is None:
+            out = torch.empty_like(node)
+        ps = parent.stride(0) if R > 1 else BW
+        ts = token.stride(0) if R > 1 else BW
+        _check(lib.xattn_trie_advance(ctypes.byref(self.layout),
+                                      ctypes.c_void_p(self.table.data_ptr()), int(depth),
+                                      _ptr(node), ctypes.c_void_p(parent.data_ptr()), ps,
+                                      ctypes.c_void_p(token.data_ptr()), ts, _ptr(out), R, BW,
+                                      _stream(stream, self.device)))
+        return out
 
 
 def _rows_out(t, R: int, BW: int, dtype, device):

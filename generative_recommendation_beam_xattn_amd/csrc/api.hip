@@ -191,9 +191,119 @@ xattn_status reorder_unshared(const xattn_shape *s, void *unshared_k, void *unsh
   return XATTN_OK;
 }
 
+xattn_status check_trie(const xattn_trie *lay, const void *table, int32_t depth) {
+  if (!lay || !table) return fail(XATTN_EINVAL, "layout and table are required");
+  if (lay->levels < 1 || lay->levels > XATTN_TRIE_MAX_LEVELS || lay->vocab < 1 ||
+      lay->vocab > 32 * xattn::kMaxMaskWords || lay->words != (lay->vocab + 31) / 32 ||
+      lay->dense_levels < 0 || lay->dense_levels > lay->levels)
+    return fail(XATTN_EINVAL, "layout is not one xattn_trie_build wrote");
+  if (depth < 0 || depth >= lay->levels) return fail(XATTN_EINVAL, "depth must be in [0, levels)");
+  if (!aligned(table, 256)) return fail(XATTN_EINVAL, "table must be 256-byte aligned");
+  return XATTN_OK;
+}
+
+xattn_status valid_mask(const xattn_trie *lay, const void *table, int32_t depth,
+                        const int32_t *node, float *logits, int32_t R, int32_t BW,
+                        int64_t row_stride, void *stream, xattn::LaunchEvents ev = {}) {
+  xattn_status st = check_trie(lay, table, depth);
+  if (st != XATTN_OK) return st;
+  if (R < 1 || BW < 1) return fail(XATTN_EINVAL, "R and BW must be >= 1");
+  if (!node || !logits) return fail(XATTN_EINVAL, "a required pointer is NULL");
+  if (row_stride < lay->vocab || row_stride % 4 != 0)
+    return fail(XATTN_EINVAL, "row_stride must be >= vocab and a multiple of 4");
+  if ((double)R * BW * row_stride > kMaxElems) return fail(XATTN_EINVAL, "logits exceed 2^40 elements");
+  if (!aligned(logits, 16)) return fail(XATTN_EINVAL, "logits must be 16-byte aligned");
+  if (!aligned(node, 4)) return fail(XATTN_EINVAL, "int32 arrays must be 4-byte aligned");
+  xattn::MaskParams p{};
+  p.table = static_cast<const uint8_t *>(table);
+  p.node = node;
+  p.logits = logits;
+  p.row_stride = row_stride;
+  p.row_ptr_off = lay->row_ptr_off[depth];
+  p.child_tok_off = lay->child_tok_off[depth];
+  p.mask_off = depth < lay->dense_levels ? lay->mask_off[depth] : 0;
+  p.R = R;
+  p.BW = BW;
+  p.V = lay->vocab;
+  p.words = lay->words;
+  p.n_nodes = lay->nodes[depth];
+  p.n_edges = lay->nodes[depth + 1];
+  p.dense = depth < lay->dense_levels ? 1 : 0;
+  hipError_t e = xattn::launch_valid_mask(p, static_cast<hipStream_t>(stream), ev);
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+xattn_status xattn_trie_build(const int32_t *items, int64_t n_items, int32_t levels,
+                              int32_t vocab, int32_t dense_levels, xattn_trie *layout,
+                              void *host_table, size_t host_bytes) {
+  if (!layout) return fail(XATTN_EINVAL, "layout is NULL");
+  const char *err = xattn::build_trie(items, n_items, levels, vocab, dense_levels, layout,
+                                      host_table, host_bytes);
+  if (err) return fail(XATTN_EINVAL, err);
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
+xattn_status xattn_valid_mask(const xattn_trie *layout, const void *table, int32_t depth,
+                              const int32_t *node, float *logits, int32_t R, int32_t BW,
+                              int64_t row_stride, void *stream) {
+  return valid_mask(layout, table, depth, node, logits, R, BW, row_stride, stream);
+}
+
+xattn_status xattn_valid_mask_timed(const xattn_trie *layout, const void *table, int32_t depth,
+                                    const int32_t *node, float *logits, int32_t R, int32_t BW,
+                                    int64_t row_stride, void *stream, void *start_event,
+                                    void *stop_event) {
+  if (!start_event || !stop_event) return fail(XATTN_EINVAL, "both timing events are required");
+  xattn::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  return valid_mask(layout, table, depth, node, logits, R, BW, row_stride, stream, ev);
+}
+
+xattn_status xattn_trie_advance(const xattn_trie *layout, const void *table, int32_t depth,
+                                const int32_t *node, const int32_t *parent,
+                                int64_t parent_stride, const int32_t *token,
+                                int64_t token_stride, int32_t *new_node, int32_t R, int32_t BW,
+                                void *stream) {
+  xattn_status st = check_trie(layout, table, depth);
+  if (st != XATTN_OK) return st;
+  if (R < 1 || BW < 1) return fail(XATTN_EINVAL, "R and BW must be >= 1");
+  if (!node || !parent || !token || !new_node) return fail(XATTN_EINVAL, "a required pointer is NULL");
+  if (parent_stride < BW || token_stride < BW)
+    return fail(XATTN_EINVAL, "parent_stride and token_stride must be >= BW");
+  if ((double)R * parent_stride > kMaxElems || (double)R * token_stride > kMaxElems ||
+      (double)R * BW > kMaxElems)
+    return fail(XATTN_EINVAL, "an array exceeds 2^40 elements");
+  const void *ptrs[] = {node, parent, token, new_node};
+  for (const void *v : ptrs)
+    if (!aligned(v, 4)) return fail(XATTN_EINVAL, "int32 arrays must be 4-byte aligned");
+  xattn::AdvanceParams p{};
+  p.table = static_cast<const uint8_t *>(table);
+  p.node = node;
+  p.parent = parent;
+  p.parent_stride = parent_stride;
+  p.token = token;
+  p.token_stride = token_stride;
+  p.new_node = new_node;
+  p.row_ptr_off = layout->row_ptr_off[depth];
+  p.child_tok_off = layout->child_tok_off[depth];
+  p.R = R;
+  p.BW = BW;
+  p.V = layout->vocab;
+  p.n_nodes = layout->nodes[depth];
+  p.n_edges = layout->nodes[depth + 1];
+  hipError_t e = xattn::launch_trie_advance(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
 
 xattn_status xattn_reorder_unshared(const xattn_shape *shape, void *unshared_k, void *unshared_v,
                                     const int32_t *parent, int64_t parent_stride,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/xbeam.h"
+
 namespace xattn {
 
 // Chains of at most this many levels are walked inside the attention kernel
@@ -74,6 +76,40 @@ struct ReorderParams {
 hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream,
                                    LaunchEvents ev = {});
 int64_t reorder_chunk_bytes(int64_t row_bytes, int32_t BW);
+
+// Valid-path tables and kernels (layout as in xbeam.h).
+using TrieLayout = xattn_trie;
+constexpr int kMaxTrieLevels = XATTN_TRIE_MAX_LEVELS;
+constexpr int kMaxMaskWords = 2048;   // vocabularies up to 65536 tokens
+
+struct MaskParams {
+  const uint8_t *table;
+  const int32_t *node;     // [R * BW] node id at the masked depth, -1 = dead
+  float *logits;           // R * BW rows of V, row stride row_stride
+  int64_t row_stride;
+  int64_t row_ptr_off, child_tok_off, mask_off;   // sections of the masked depth
+  int32_t R, BW, V, words, n_nodes, n_edges;   // nodes at depth d and d + 1
+  int32_t dense;           // 1: the depth has dense bit rows
+};
+
+struct AdvanceParams {
+  const uint8_t *table;
+  const int32_t *node;     // [R][BW] nodes at depth d
+  const int32_t *parent;   // [R] rows of BW, stride parent_stride
+  int64_t parent_stride;
+  const int32_t *token;    // [R] rows of BW, stride token_stride
+  int64_t token_stride;
+  int32_t *new_node;       // [R][BW] nodes at depth d + 1
+  int64_t row_ptr_off, child_tok_off;             // sections of depth d
+  int32_t R, BW, V, n_nodes, n_edges;             // nodes at depth d and d + 1
+};
+
+hipError_t launch_valid_mask(const MaskParams &p, hipStream_t stream, LaunchEvents ev = {});
+hipError_t launch_trie_advance(const AdvanceParams &p, hipStream_t stream);
+// Host: lay out (and, with host_table, fill) the tables; nullptr or a reason.
+const char *build_trie(const int32_t *items, int64_t n_items, int32_t levels, int32_t vocab,
+                       int32_t dense_levels, TrieLayout *lay, void *host_table,
+                       size_t host_bytes);
 
 // Beam selection: the BW best of BW x V sorted candidates per request.
 hipError_t launch_beam_topk(const float *cum, const float *logp, const int32_t *tok, int32_t R,
