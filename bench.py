@@ -21,8 +21,10 @@ the duration is the kernel's own, as a kernel trace reports it.
 sample of the same workload.  After the timed region, two side legs time
 other kernels on the same device: `per_beam_comparison` (the per-beam
 PagedAttention-style kernel on the same inputs), `beam_selection` (the
-top-BW beam selection on the workload's BW x BW candidate pool) and
-`unshared_reorder` (the in-place Unshared-cache reorder at each level).
+top-BW beam selection on the workload's BW x BW candidate pool),
+`unshared_reorder` (the in-place Unshared-cache reorder at each level) and
+`valid_path_mask` (masking the workload's beams' logits over a 2^20-item
+vocabulary at each depth).
 """
 from __future__ import annotations
 
@@ -67,6 +69,9 @@ def parse():
     ap.add_argument("--reorder-steps", type=int, default=20,
                     help="rounds of the in-place Unshared reorder timed after the main run, on "
                          "the rotation copies (0 skips it)")
+    ap.add_argument("--mask-steps", type=int, default=20,
+                    help="rounds of valid-path masking timed after the main run, per depth, on "
+                         "the workload's beams over the full item vocabulary (0 skips it)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -208,6 +213,67 @@ def reorder_leg(w, copies, steps: int, stream) -> dict | None:
         by_level.append({"level": s, "levels_moved": s, "kernel_us": t, "bytes": byts,
                          "GBps": byts / t / 1e3, "frac_of_hbm_peak": byts / t / 1e3 / HBM_PEAK_GBS})
     return {"by_level": by_level, "bound": "hbm", "steps": steps}
+
+
+# ------------------------------------------------------------ valid-path masks
+
+def valid_mask_leg(w, steps: int, dev, stream) -> dict | None:
+    """xattn_valid_mask on R x BW beams of the workload over the full item
+    vocabulary (2^20 items of 3 tokens over 8192 ids; dense masks at depths
+    0 and 1, sparse at 2), at every depth, on logits rotated through enough
+    buffers (>= 512 MB) to come from HBM.  Beams sit on prefixes of random
+    items (one in ten random, mostly dead).  Algorithmic bytes per launch:
+    4 B per slot that becomes -inf, 16 B read per 4-slot group that mixes
+    valid and invalid slots, and each distinct node's mask row (dense) or
+    children (sparse) once."""
+    import torch
+    from generative_recommendation_beam_xattn_amd import binding as B
+    from generative_recommendation_beam_xattn_amd import workloads as W
+    c = W.VALID_ITEMS_FULL
+    R, BW, V, L = w.R, w.BW, c["vocab"], c["levels"]
+    items = W.valid_items(42, **c)
+    vp = B.ValidPaths(items, V, 2, device=dev)
+    rng = np.random.default_rng(5)
+    row_bytes = R * BW * V * 4
+    n_buf = max(2, min(16, -(-512 * 2**20 // row_bytes)))
+    bufs = [torch.empty((R, BW, V), dtype=torch.float32, device=dev) for _ in range(n_buf)]
+    for b in bufs:
+        b.normal_()
+    ident = torch.arange(BW, dtype=torch.int32, device=dev).repeat(R, 1).contiguous()
+    pick = rng.integers(0, len(items), size=R * BW)
+    rand = rng.random(R * BW) < 0.1
+    paths = np.where(rand[:, None], rng.integers(0, V, size=(R * BW, L)), items[pick])
+    node = vp.root(R, BW)
+    out = []
+    for depth in range(L):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps + 1)]
+        for a, b in ev:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for k in range(steps + 1):       # round 0 is a warmup
+            vp.mask(depth, node, bufs[k % n_buf], stream=stream, events=ev[k])
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev[1:]]) * 1e3)
+        fin = torch.isfinite(bufs[0]).view(R * BW, V // 4, 4).sum(dim=2).cpu().numpy()
+        n_valid = int(fin.sum())
+        mixed = int(np.sum((fin > 0) & (fin < 4)))
+        nodes = np.unique(node.cpu().numpy())
+        nodes = nodes[nodes >= 0]
+        if depth < vp.layout.dense_levels:
+            table_bytes = len(nodes) * vp.layout.words * 4
+        else:
+            table_bytes = 8 * len(nodes) + 4 * n_valid
+        byts = 4 * (R * BW * V - n_valid) + 16 * mixed + table_bytes
+        out.append({"depth": depth, "dense": depth < vp.layout.dense_levels, "kernel_us": us,
+                    "valid_slots": n_valid, "bytes": byts, "GBps": byts / us / 1e3,
+                    "frac_of_hbm_peak": byts / us / 1e3 / HBM_PEAK_GBS})
+        tok = torch.from_numpy(paths[:, depth].astype(np.int32).reshape(R, BW)).to(dev)
+        node = vp.advance(depth, node, ident, tok)
+    torch.cuda.synchronize()
+    return {"beams": {"R": R, "BW": BW}, "vocab": V, "items": c["n_items"],
+            "by_depth": out, "bound": "hbm", "buffers": n_buf, "steps": steps}
 
 
 # ------------------------------------------------------------ beam selection
@@ -352,6 +418,7 @@ def main():
 
     beam_sel = beam_selection_leg(w, args.topk_steps, dev) if args.topk_steps > 0 else None
     reorder = reorder_leg(w, copies, args.reorder_steps, stream) if args.reorder_steps > 0 else None
+    masks = valid_mask_leg(w, args.mask_steps, dev, stream) if args.mask_steps > 0 else None
 
     t_kernel = float(mean_launch_s.mean())
     bytes_per_launch = float(np.mean([x["bytes"] for x in work]))
@@ -401,6 +468,7 @@ def main():
         "per_beam_comparison": per_beam,
         "beam_selection": beam_sel,
         "unshared_reorder": reorder,
+        "valid_path_mask": masks,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
