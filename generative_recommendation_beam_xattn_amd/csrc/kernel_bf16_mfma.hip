@@ -137,6 +137,22 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
       : "memory");
 }
 
+// The same for 4 bytes per lane (global_load_lds_dword): lane i's 4 bytes
+// at src land at LDS byte address lds_base + 4 i.
+__device__ __forceinline__ void dma4(const void *src, const void *lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+}
+
 // Workgroup barrier that also orders this wave's LDS accesses in the
 // compiler, without the vmcnt(0) a full fence would impose on the tile
 // copies still in flight.  Callers wait for the copies they need first.
@@ -355,11 +371,17 @@ __device__ __forceinline__ void softmax_exp(f32x16 (&sacc)[2 / KSPLIT], bf16x8 (
   }
 }
 
+// LDS fragment reads kept in flight ahead of the MFMA that consumes them: an
+// LDS read takes longer than one MFMA plus its share of VALU work, so with
+// one read ahead every MFMA waited on it.
+constexpr int kFragAhead = 2;
+
 // The S^T MFMAs of the next tile interleaved, k-step by k-step, with part 2
-// of the current tile's softmax: each k-step prefetches the next K
-// fragment, issues its MFMA(s) and then a share of the exponentials, their
-// bf16 packing and row sum, so the VALU works while the matrix core runs.
-// sched_barrier fences keep that order through scheduling.
+// of the current tile's softmax: each k-step issues the read of the K
+// fragment kFragAhead steps on, its MFMA(s) and then a share of the
+// exponentials, their bf16 packing and row sum, so the VALU works while the
+// matrix core runs.  sched_barrier fences keep that order through
+// scheduling.
 template <int D, int KSPLIT>
 __device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf16x8 (&qf)[D / 16],
                                                  f32x16 (&s_next)[2 / KSPLIT],
@@ -374,20 +396,22 @@ __device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf1
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int i = 0; i < NKB; ++i) s_next[i] = f32x16{};
-  bf16x8 a_cur[NKB];
+  bf16x8 a[NKS][NKB];   // indexed by unrolled constants only: registers
 #pragma unroll
-  for (int i = 0; i < NKB; ++i)
-    a_cur[i] = *reinterpret_cast<const bf16x8 *>(ktile + fo.k[0] + i * 32 * Gm::RB);
+  for (int j = 0; j < kFragAhead && j < NKS; ++j)
+#pragma unroll
+    for (int i = 0; i < NKB; ++i)
+      a[j][i] = *reinterpret_cast<const bf16x8 *>(ktile + fo.k[j] + i * 32 * Gm::RB);
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    bf16x8 a_nxt[NKB];
-    if (ks + 1 < NKS) {
+    if (ks + kFragAhead < NKS) {
 #pragma unroll
       for (int i = 0; i < NKB; ++i)
-        a_nxt[i] = *reinterpret_cast<const bf16x8 *>(ktile + fo.k[ks + 1] + i * 32 * Gm::RB);
+        a[ks + kFragAhead][i] =
+            *reinterpret_cast<const bf16x8 *>(ktile + fo.k[ks + kFragAhead] + i * 32 * Gm::RB);
     }
 #pragma unroll
-    for (int i = 0; i < NKB; ++i) s_next[i] = mfma(a_cur[i], qf[ks], s_next[i]);
+    for (int i = 0; i < NKB; ++i) s_next[i] = mfma(a[ks][i], qf[ks], s_next[i]);
 #pragma unroll
     for (int u = 0; u < PER; u += 2) {
       const int v = ks * PER + u;      // score index: block v / 16, element v % 16
@@ -399,10 +423,6 @@ __device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf1
       st.l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, st.l, false);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (ks + 1 < NKS) {
-#pragma unroll
-      for (int i = 0; i < NKB; ++i) a_cur[i] = a_nxt[i];
-    }
   }
 }
 
@@ -428,14 +448,14 @@ __device__ __forceinline__ void pv_tile(const uint8_t *vt, const bf16x8 (&pf)[4 
         (lds_bf16x4 *)(vbase + fo.v[1][db] + prow * Gm::RB));
     return bf16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
   };
-  bf16x8 a_cur = frag(0);
+  bf16x8 a[NSTEP];   // indexed by unrolled constants only: registers
+#pragma unroll
+  for (int j = 0; j < kFragAhead && j < NSTEP; ++j) a[j] = frag(j);
 #pragma unroll
   for (int n = 0; n < NSTEP; ++n) {
-    bf16x8 a_nxt;
-    if (n + 1 < NSTEP) a_nxt = frag(n + 1);
-    st.O[n % NDB] = mfma(a_cur, pf[n / NDB], st.O[n % NDB]);
+    if (n + kFragAhead < NSTEP) a[n + kFragAhead] = frag(n + kFragAhead);
+    st.O[n % NDB] = mfma(a[n], pf[n / NDB], st.O[n % NDB]);
     __builtin_amdgcn_sched_barrier(0);
-    if (n + 1 < NSTEP) a_cur = a_nxt;
   }
 }
 
@@ -713,7 +733,6 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   constexpr int NKB = 2 / KSPLIT;       // 32-key blocks per wave per tile
   using Gm = TileGeom<D>;
   constexpr int CPW = Gm::COPIES / WAVES;   // wave-wide copies per wave per tile
-  constexpr int PPT = (kParentLdsInts + NT - 1) / NT;  // staged parent ints per thread
 
   // The tile ring: K tiles of stages 0..3, then V tiles of stages 0..3, in
   // one LDS object at constant offsets.  Constant offsets let every
@@ -738,9 +757,12 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int rb = lb % p.n_rb;
   const int unit = lb / p.n_rb;
-  const int r = unit / p.Hkv;
+  const int r = __builtin_amdgcn_readfirstlane(unit / p.Hkv);
   const int k = unit % p.Hkv;
   const int G = p.G, BW = p.BW, step = p.step;
+  // the prompt length first, before any copy is issued: a scalar load whose
+  // wait does not involve the vector-memory counter the copies run on
+  const int L = clampi(p.prompt_len[r], 0, p.Lmax);
   const float c = p.scale_log2;
   // in raw dot-product units; the debug variant reports the stages' true
   // maxima, so it raises m on every increase
@@ -754,16 +776,18 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   const bool walk_here = p.anc == nullptr;
   const bool staged = walk_here && stage_parents_in_lds(step, BW);
 
-  // ---- loads that depend on nothing, oldest first (vmcnt counts in
-  // order): parent rows for the walk, this wave's q rows
-  int32_t pv[PPT];
+  // ---- copies into LDS that depend on nothing, issued before the tile
+  // copies (vmcnt counts in issue order, so the wait for tile 0 covers
+  // them): the parent rows of levels 1..step for the walk, and the q rows of
+  // each row group -- its key-half-0 wave copies them into ring stage 3,
+  // which no tile uses before the first loop step, and both waves of the
+  // group read them from there.  No vector load the compiler sees is in
+  // flight, so it adds no wait of its own for them.
   const int32_t *par = p.parent_idx + (int64_t)r * p.S * BW;
   if (staged) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int e = tid + i * NT;
-      pv[i] = e < step * BW ? par[BW + e] : 0;   // levels 1..step
-    }
+    const int n_par = step * BW;
+    for (int c0 = wave * 64; c0 < n_par; c0 += WAVES * 64)
+      dma4(par + BW + min(c0 + lane, n_par - 1), par_lds + c0);
   }
   const uint16_t *qg = static_cast<const uint16_t *>(p.q);
   uint16_t *og = static_cast<uint16_t *>(p.out);
@@ -772,11 +796,14 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   const int rr = valid ? row : p.M - 1;
   const int beam = rr / G;
   const int64_t qoff = (((int64_t)r * BW + beam) * p.Hq + k * G + rr % G) * D;
-  bf16x8 qf[NKS];
+  // stage 3 holds the q rows of row groups 0, 1 (K buffer) and 2, 3 (V
+  // buffer): NKS 1 KiB fragments per group, lane i's 16 bytes at 16 i
+  const uint8_t *qlds = tiles + ((rg < 2 ? 3 : NSTAGE + 3) * Gm::TILE_BYTES) +
+                        (rg & 1) * (NKS * 1024);
+  if (kh == 0) {
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = __builtin_bit_cast(bf16x8,
-                                *reinterpret_cast<const uint4 *>(qg + qoff + ks * 16 + hl * 8));
+    for (int ks = 0; ks < NKS; ++ks) dma16(qg + qoff + ks * 16 + hl * 8, qlds + ks * 1024);
+  }
 
   const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
                         ((int64_t)r * p.Hkv + k) * p.S * BW * D;
@@ -801,7 +828,6 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       tile_copy<D, WAVES, false>(tiles + i * Gm::TILE_BYTES, tiles + (NSTAGE + i) * Gm::TILE_BYTES,
                                  cplan, skg, svg, i * KT, 0, wave);
   }
-  const int L = clampi(p.prompt_len[r], 0, p.Lmax);
   const int n_tiles = (L + KT - 1) / KT;
   // Tile t covers keys [t*KT, t*KT + KT); the last one's window is shifted
   // back to [L - KT, L) (when L >= KT) so that no copy needs clamping; its
@@ -855,15 +881,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     wait_vm_lgkm0<CPW>();
   else
     wait_vm_lgkm0<0>();
-  if (staged) {
-#pragma unroll
-    for (int i = 0; i < PPT; ++i) {
-      const int e = tid + i * NT;
-      if (e < step * BW) par_lds[e] = pv[i];
-    }
-    wait_vm_lgkm0<63>();  // lgkmcnt only
-    lds_barrier();
-  }
+  if (staged) lds_barrier();   // every wave's parent copies have landed
   if (walk_here) {
     for (int i = tid; i < nb; i += NT) {
       int a = b_lo + i;
@@ -875,7 +893,11 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       }
     }
   }
-  lds_barrier();  // tile 0 and the ancestor slots are visible
+  lds_barrier();  // tile 0, q and the ancestor slots are visible
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8 *>(qlds + ks * 1024 + lane * 16);
   // rows of the two chunks the loop may copy (the last two steps), read
   // from LDS now, while no copy into LDS is in flight
   constexpr int B0PW = block0_copies_per_wave<D, WAVES>();
@@ -1149,7 +1171,9 @@ hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream, LaunchEvents e
   if (p.anc == nullptr) {
     const int nb = min(p.BW, (ROWS - 1) / p.G + 2);
     dyn = (size_t)nb * (p.step + 1) * sizeof(int32_t);
-    if (stage_parents_in_lds(p.step, p.BW)) dyn += (size_t)p.step * p.BW * sizeof(int32_t);
+    // parent rows are copied 64 ints per wave instruction: whole rounds of 64
+    if (stage_parents_in_lds(p.step, p.BW))
+      dyn += (size_t)((p.step * p.BW + 63) / 64 * 64) * sizeof(int32_t);
   }
   if (ev.start)
     hipExtLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
