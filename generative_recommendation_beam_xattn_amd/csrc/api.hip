@@ -124,7 +124,7 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   }
   if (s->dtype == XATTN_F32)
     e = xattn::launch_decode_f32(p, hs, ev);  // per query row already: also the per-beam form
-  else if (per_beam)
+  else if (per_beam || (!taps && p.M <= xattn::kPerBeamMaxRows))
     e = xattn::launch_decode_per_beam_bf16(p, hs, ev);
   else
     e = xattn::launch_decode_bf16(p, taps, hs, ev);

@@ -13,6 +13,13 @@ namespace xattn {
 // the workspace first.
 constexpr int kMaxInKernelLevels = 16;
 
+// With this few query rows per (request, KV head) -- one or two beams -- the
+// staged kernel's 32-row MFMA blocks are mostly empty and there is almost
+// nothing to share; the per-beam kernel runs those calls (measured on the
+// prefix-sharing shapes: 1079 vs 2903 us at 4 rows, 957 vs 1498 us at 8,
+// and the staged kernel ahead from 16 rows).
+constexpr int kPerBeamMaxRows = 8;
+
 // Largest beam width the beam-selection kernel takes.
 constexpr int kMaxTopkBeams = 512;
 // Largest beam width the Unshared-cache reorder takes.

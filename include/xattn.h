@@ -87,6 +87,10 @@ typedef struct {
  *                                     rows 1..step are read, row 0 never
  *   step        0 <= step < S         current level s
  *   out         [R][BW][Hq][D]        written, same dtype as q
+ *   (Calls with at most 8 query rows per request and KV head -- BW * Hq / Hkv
+ *   <= 8, i.e. one or two beams -- are run by the per-beam kernel described
+ *   below: with so few rows there is nothing to share, and the result is the
+ *   same within rounding.)
  *   workspace   device scratch of at least xattn_workspace_size(shape, step)
  *               bytes, 256-byte aligned; may be NULL when that size is 0.
  *               Its contents on entry are ignored; two calls in flight at

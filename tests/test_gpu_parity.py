@@ -48,6 +48,10 @@ SMALL = {
     "deep_chain_wide": dict(R=1, BW=300, Hq=4, Hkv=4, D=64, L=[65], steps=[20], S=24),
     "single_beam_empty_prompt": dict(R=2, BW=1, Hq=4, Hkv=1, D=128, L=[0, 0], steps=[0]),
     "no_shared_rows": dict(R=2, BW=3, Hq=4, Hkv=2, D=64, L=[0, 0], steps=[1], Lmax=0),
+    # either side of the row count below which bf16 calls go to the per-beam
+    # kernel (8 query rows per request and KV head)
+    "rows8_per_beam_path": dict(R=3, BW=2, Hq=8, Hkv=2, D=128, L=[70, 0, 333], steps=[0, 2], S=3),
+    "rows9_staged_path": dict(R=3, BW=3, Hq=6, Hkv=2, D=128, L=[70, 0, 333], steps=[0, 2], S=3),
 }
 
 
