@@ -54,10 +54,25 @@ xattn_status check_shape(const xattn_shape *s, int32_t step) {
 
 bool deep_chain(int32_t step) { return step + 1 > xattn::kMaxInKernelLevels; }
 
-size_t workspace_bytes_for(const xattn_shape *s, int32_t step) {
-  if (!deep_chain(step)) return 0;
+// Workspace of a deep-chain call: the resolved ancestor slots, then (bf16)
+// the Unshared-stage partials of every query row, (m, l) and o [D] in float.
+size_t anc_bytes_for(const xattn_shape *s, int32_t step) {
   const size_t n = (size_t)s->num_requests * (size_t)(step + 1) * (size_t)s->beam_width;
   return (n * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
+size_t rows_of(const xattn_shape *s) {
+  return (size_t)s->num_requests * (size_t)s->beam_width * (size_t)s->num_q_heads;
+}
+
+size_t workspace_bytes_for(const xattn_shape *s, int32_t step) {
+  if (!deep_chain(step)) return 0;
+  size_t bytes = anc_bytes_for(s, step);
+  if (s->dtype == XATTN_BF16) {
+    bytes += (rows_of(s) * 2 * sizeof(float) + 255) & ~size_t(255);
+    bytes += (rows_of(s) * (size_t)s->head_dim * sizeof(float) + 255) & ~size_t(255);
+  }
+  return bytes;
 }
 
 xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, const void *shared_v,
@@ -112,22 +127,47 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   p.scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)p.D);
   p.scale_log2 = p.scale * 1.4426950408889634f;
   p.anc = nullptr;
+  p.tok_ml = nullptr;
+  p.tok_o = nullptr;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  // timing events: start bound to the call's first kernel, stop to its last
+  xattn::LaunchEvents ev_first{ev.start, nullptr}, ev_last{nullptr, ev.stop};
+  bool first = true;
+  auto first_ev = [&]() {
+    xattn::LaunchEvents r = first ? ev_first : xattn::LaunchEvents{};
+    first = false;
+    return r;
+  };
   if (need > 0) {
     int32_t *anc = static_cast<int32_t *>(workspace);
     const xattn::AncLayout lay{(int64_t)(step + 1) * p.BW, 1, p.BW};  // [R][step+1][BW]
-    e = xattn::launch_resolve_ancestors(parent_idx, p.R, p.BW, p.S, step, anc, lay, hs);
+    e = xattn::launch_resolve_ancestors(parent_idx, p.R, p.BW, p.S, step, anc, lay, hs,
+                                        first_ev());
     if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
     p.anc = anc;
   }
+  const bool staged_bf16 =
+      s->dtype == XATTN_BF16 && !per_beam && (taps || p.M > xattn::kPerBeamMaxRows);
+  if (need > 0 && staged_bf16 && !taps) {
+    // deep chains: the Unshared stage runs first with one workgroup per
+    // (request, beam, KV head), so the gather of every beam's token rows
+    // spreads over the whole GPU; the staged kernel starts from its partials
+    uint8_t *w = static_cast<uint8_t *>(workspace) + anc_bytes_for(s, step);
+    p.tok_ml = reinterpret_cast<float *>(w);
+    p.tok_o = reinterpret_cast<float *>(w + ((rows_of(s) * 2 * sizeof(float) + 255) &
+                                             ~size_t(255)));
+    e = xattn::launch_token_partials_bf16(p, hs, first_ev());
+    if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  }
+  xattn::LaunchEvents ev_main = first ? ev : ev_last;
   if (s->dtype == XATTN_F32)
-    e = xattn::launch_decode_f32(p, hs, ev);  // per query row already: also the per-beam form
-  else if (per_beam || (!taps && p.M <= xattn::kPerBeamMaxRows))
-    e = xattn::launch_decode_per_beam_bf16(p, hs, ev);
+    e = xattn::launch_decode_f32(p, hs, ev_main);  // per query row already: also the per-beam form
+  else if (!staged_bf16)
+    e = xattn::launch_decode_per_beam_bf16(p, hs, ev_main);
   else
-    e = xattn::launch_decode_bf16(p, taps, hs, ev);
+    e = xattn::launch_decode_bf16(p, taps, hs, ev_main);
   if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
   g_last_error[0] = '\0';
   return XATTN_OK;

@@ -8,6 +8,8 @@
 // One thread follows one beam.  Parent rows are staged through LDS a chunk
 // of levels at a time with coalesced loads, so each step of the walk is a
 // dependent LDS read rather than a dependent global-memory round trip.
+#include <hip/hip_ext.h>
+
 #include "xattn_internal.h"
 
 namespace xattn {
@@ -58,18 +60,19 @@ __global__ __launch_bounds__(kThreads) void resolve_ancestors_kernel(
 
 hipError_t launch_resolve_ancestors(const int32_t *parent_idx, int32_t R, int32_t BW, int32_t S,
                                     int32_t step, int32_t *anc, AncLayout layout,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, LaunchEvents ev) {
   const int32_t bpr = (BW + kThreads - 1) / kThreads;
   const int64_t grid = (int64_t)R * bpr;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (BW <= kLdsInts) {
-    const int32_t chunk = max(1, min(step, kLdsInts / BW));
-    hipLaunchKernelGGL(resolve_ancestors_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0,
-                       stream, parent_idx, BW, S, step, anc, layout, bpr, chunk);
-  } else {
-    hipLaunchKernelGGL(resolve_ancestors_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0,
-                       stream, parent_idx, BW, S, step, anc, layout, bpr, 1);
-  }
+  const bool lds = BW <= kLdsInts;
+  const int32_t chunk = lds ? max(1, min(step, kLdsInts / BW)) : 1;
+  auto kernel = lds ? resolve_ancestors_kernel<true> : resolve_ancestors_kernel<false>;
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0u, stream, ev.start,
+                          ev.stop, 0u, parent_idx, BW, S, step, anc, layout, bpr, chunk);
+  else
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, parent_idx, BW,
+                       S, step, anc, layout, bpr, chunk);
   return hipGetLastError();
 }
 

@@ -794,7 +794,7 @@ hipError_t launch_beam_topk(const float *cum, const float *logp, const int32_t *
   TopkArgs a{cum, logp, tok, score, parent, token, out_stride, BW, V,
              beam_topk_sample_len(BW, V), beam_topk_short_len(BW, V)};
   static_assert(kMaxBW * 8 <= kShortSample && kShortSample <= kSampleCap, "short sample size");
-  if (ev.start)
+  if (ev.start || ev.stop)
     hipExtLaunchKernelGGL(beam_topk_kernel, dim3((unsigned)R), dim3(kThreads), 0u, stream,
                           ev.start, ev.stop, 0u, a);
   else

@@ -922,9 +922,32 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     // deep chains: key half kh takes levels step - kh, step - kh - 2, ...;
     // the state seeds the online softmax the prompt tiles continue
     if (!walk_here) {
-      TokenRows<D> none;
-      unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step - kh, KSPLIT,
-                         c, lane, none, false);
+      if (p.tok_o) {
+        // the Unshared stage was computed beforehand, one workgroup per
+        // (request, beam, KV head): start from its partial; key half 1
+        // starts empty, and l lives in lane half 0 (the row total is the
+        // pair's sum)
+        if (kh == 0) {
+          const int64_t ro = qoff / D;
+          st.m = p.tok_ml[ro * 2 + 0];
+          st.l = hl == 0 ? p.tok_ml[ro * 2 + 1] : 0.f;
+          const float *po = p.tok_o + ro * D;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float4 v = *reinterpret_cast<const float4 *>(po + db * 32 + 8 * j + 4 * hl);
+              st.O[db][4 * j + 0] = v.x;
+              st.O[db][4 * j + 1] = v.y;
+              st.O[db][4 * j + 2] = v.z;
+              st.O[db][4 * j + 3] = v.w;
+            }
+        }
+      } else {
+        TokenRows<D> none;
+        unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step - kh, KSPLIT,
+                           c, lane, none, false);
+      }
     }
   }
 
@@ -1175,7 +1198,7 @@ hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream, LaunchEvents e
     if (stage_parents_in_lds(p.step, p.BW))
       dyn += (size_t)((p.step * p.BW + 63) / 64 * 64) * sizeof(int32_t);
   }
-  if (ev.start)
+  if (ev.start || ev.stop)
     hipExtLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
                           dim3(RG * KSPLIT * 64), (uint32_t)dyn, stream, ev.start, ev.stop, 0u, p);
   else

@@ -171,7 +171,7 @@ namespace {
 
 template <int D>
 void launch_f32_d(const DecodeParams &p, unsigned grid, hipStream_t stream, LaunchEvents ev) {
-  if (ev.start)
+  if (ev.start || ev.stop)
     hipExtLaunchKernelGGL(decode_f32_kernel<D>, dim3(grid), dim3(kWaves * 64), 0u, stream,
                           ev.start, ev.stop, 0u, p);
   else

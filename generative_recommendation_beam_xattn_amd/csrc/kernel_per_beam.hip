@@ -27,16 +27,21 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerPass = 4;   // query rows a pass keeps state for
+constexpr int kAncLds = 2048;     // ancestor slots staged in LDS (levels)
+constexpr int kKeysInFlight = 4;  // keys per lane group whose loads go out together
 
 __device__ inline float lo_f(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ inline float hi_f(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-template <int D>
+// TOKENS: the Unshared stage alone (keys = the beam's tokens at levels
+// 0..step), written as an online-softmax partial for the staged kernel to
+// start from, instead of normalised output.
+template <int D, bool TOKENS>
 __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodeParams p) {
   constexpr int LPK = D / 8;        // lanes per key row
   constexpr int KPW = 64 / LPK;     // key rows per wave per load
   constexpr int NSG = kWaves * KPW; // lane groups in the workgroup
-  __shared__ int32_t anc_s[kMaxInKernelLevels];
+  __shared__ int32_t anc_s[kAncLds];
   __shared__ float red_o[NSG][kRowsPerPass][D];
   __shared__ float red_ml[NSG][kRowsPerPass][2];
 
@@ -63,11 +68,20 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
     }
     __syncthreads();
   }
+  // resolved slots (deep chains) are staged in LDS too when they fit, so a
+  // token row's address waits on an LDS read, not a global one
+  const bool anc_in_lds = p.anc == nullptr || step + 1 <= kAncLds;
+  if (p.anc && anc_in_lds) {
+    for (int t = tid; t <= step; t += kWaves * 64)
+      anc_s[t] = min(max(p.anc[((int64_t)r * (step + 1) + t) * BW + b], 0), BW - 1);
+    __syncthreads();
+  }
   auto anc_of = [&](int t) {
-    return p.anc ? min(max(p.anc[((int64_t)r * (step + 1) + t) * BW + b], 0), BW - 1) : anc_s[t];
+    return anc_in_lds ? anc_s[t]
+                      : min(max(p.anc[((int64_t)r * (step + 1) + t) * BW + b], 0), BW - 1);
   };
 
-  const int L = min(max(p.prompt_len[r], 0), p.Lmax);
+  const int L = TOKENS ? 0 : min(max(p.prompt_len[r], 0), p.Lmax);
   const int n_keys = L + step + 1;
   const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
                         ((int64_t)r * p.Hkv + k) * p.Lmax * D;
@@ -98,41 +112,52 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[j][e] = 0.f;
     }
-    for (int i = sg; i < n_keys; i += NSG) {
-      const uint16_t *kr, *vr;
-      if (i < L) {
-        kr = skg + (int64_t)i * D;
-        vr = svg + (int64_t)i * D;
-      } else {
-        const int t = i - L;
-        const int64_t e = ((int64_t)t * BW + anc_of(t)) * D;
-        kr = ukg + e;
-        vr = uvg + e;
+    // a lane group's keys sg, sg + NSG, ...: kKeysInFlight of them at a
+    // time, their K and V loads all issued before the first is used
+    for (int i0 = sg; i0 < n_keys; i0 += NSG * kKeysInFlight) {
+      uint4 kvu[kKeysInFlight], vvu[kKeysInFlight];
+#pragma unroll
+      for (int u = 0; u < kKeysInFlight; ++u) {
+        const int i = min(i0 + u * NSG, n_keys - 1);   // past the end: a valid row, unused
+        const uint16_t *kr, *vr;
+        if (i < L) {
+          kr = skg + (int64_t)i * D;
+          vr = svg + (int64_t)i * D;
+        } else {
+          const int t = i - L;
+          const int64_t e = ((int64_t)t * BW + anc_of(t)) * D;
+          kr = ukg + e;
+          vr = uvg + e;
+        }
+        kvu[u] = *reinterpret_cast<const uint4 *>(kr + part * 8);
+        vvu[u] = *reinterpret_cast<const uint4 *>(vr + part * 8);
       }
-      const uint4 kv = *reinterpret_cast<const uint4 *>(kr + part * 8);
-      const uint4 vv = *reinterpret_cast<const uint4 *>(vr + part * 8);
-      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-      for (int j = 0; j < kRowsPerPass; ++j) {
-        const uint32_t qw[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
-        float s = 0.f;
+      for (int u = 0; u < kKeysInFlight; ++u) {
+        if (i0 + u * NSG >= n_keys) break;   // the lane group's keys are done
+        const uint32_t kw[4] = {kvu[u].x, kvu[u].y, kvu[u].z, kvu[u].w};
+        const uint32_t vw[4] = {vvu[u].x, vvu[u].y, vvu[u].z, vvu[u].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[e]),
-                                              __builtin_bit_cast(bf16x2, kw[e]), s, false);
+        for (int j = 0; j < kRowsPerPass; ++j) {
+          const uint32_t qw[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
+          float s = 0.f;
 #pragma unroll
-        for (int w = LPK / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPK);
-        // online softmax of this lane group's keys (scores in exp2 units)
-        const float mn = fmaxf(m[j], s);
-        const float alpha = __builtin_amdgcn_exp2f((m[j] - mn) * c);   // 0 while m is -inf
-        const float pr = __builtin_amdgcn_exp2f((s - mn) * c);
-        m[j] = mn;
-        l[j] = l[j] * alpha + pr;
+          for (int e = 0; e < 4; ++e)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[e]),
+                                                __builtin_bit_cast(bf16x2, kw[e]), s, false);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[j][2 * e] = fmaf(o[j][2 * e], alpha, pr * lo_f(vw[e]));
-          o[j][2 * e + 1] = fmaf(o[j][2 * e + 1], alpha, pr * hi_f(vw[e]));
+          for (int w = LPK / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPK);
+          // online softmax of this lane group's keys (scores in exp2 units)
+          const float mn = fmaxf(m[j], s);
+          const float alpha = __builtin_amdgcn_exp2f((m[j] - mn) * c);   // 0 while m is -inf
+          const float pr = __builtin_amdgcn_exp2f((s - mn) * c);
+          m[j] = mn;
+          l[j] = l[j] * alpha + pr;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[j][2 * e] = fmaf(o[j][2 * e], alpha, pr * lo_f(vw[e]));
+            o[j][2 * e + 1] = fmaf(o[j][2 * e + 1], alpha, pr * hi_f(vw[e]));
+          }
         }
       }
     }
@@ -160,8 +185,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
         ot += red_o[g][j][d] * w;
       }
       const int hh = k * G + h0 + j;
-      og[(((int64_t)r * BW + b) * p.Hq + hh) * D + d] =
-          __builtin_bit_cast(uint16_t, (__bf16)(ot / lt));
+      const int64_t ro = ((int64_t)r * BW + b) * p.Hq + hh;
+      if constexpr (TOKENS) {
+        p.tok_o[ro * D + d] = ot;
+        if (d == 0) {
+          p.tok_ml[ro * 2 + 0] = mm;
+          p.tok_ml[ro * 2 + 1] = lt;
+        }
+      } else {
+        og[ro * D + d] = __builtin_bit_cast(uint16_t, (__bf16)(ot / lt));
+      }
     }
     __syncthreads();
   }
@@ -174,16 +207,36 @@ hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream
   const int64_t grid = (int64_t)p.R * p.BW * p.Hkv;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   auto go = [&](auto kernel) {
-    if (ev.start)
+    if (ev.start || ev.stop)
       hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0u, stream,
                             ev.start, ev.stop, 0u, p);
     else
       hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
   };
   if (p.D == 64)
-    go(decode_per_beam_kernel<64>);
+    go(decode_per_beam_kernel<64, false>);
   else if (p.D == 128)
-    go(decode_per_beam_kernel<128>);
+    go(decode_per_beam_kernel<128, false>);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_token_partials_bf16(const DecodeParams &p, hipStream_t stream,
+                                      LaunchEvents ev) {
+  const int64_t grid = (int64_t)p.R * p.BW * p.Hkv;
+  if (grid > 0x7fffffff || !p.anc || !p.tok_ml || !p.tok_o) return hipErrorInvalidConfiguration;
+  auto go = [&](auto kernel) {
+    if (ev.start || ev.stop)
+      hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0u, stream,
+                            ev.start, ev.stop, 0u, p);
+    else
+      hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, p);
+  };
+  if (p.D == 64)
+    go(decode_per_beam_kernel<64, true>);
+  else if (p.D == 128)
+    go(decode_per_beam_kernel<128, true>);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -85,7 +85,7 @@ hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, L
       (int64_t)p.BW * p.chunk_bytes > kStageBytes || p.chunk_bytes % 16 != 0 ||
       p.row_bytes % p.chunk_bytes != 0)
     return hipErrorInvalidConfiguration;
-  if (ev.start)
+  if (ev.start || ev.stop)
     hipExtLaunchKernelGGL(reorder_unshared_kernel, dim3((unsigned)grid), dim3(kThreads),
                           (size_t)p.BW * sizeof(int32_t), stream, ev.start, ev.stop, 0u, p);
   else

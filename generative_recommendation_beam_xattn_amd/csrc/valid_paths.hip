@@ -123,7 +123,7 @@ hipError_t launch_valid_mask(const MaskParams &p, hipStream_t stream, LaunchEven
   const int64_t grid = (int64_t)p.R * p.BW;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff || p.words > kMaxMaskWords) return hipErrorInvalidConfiguration;
-  if (ev.start)
+  if (ev.start || ev.stop)
     hipExtLaunchKernelGGL(valid_mask_kernel, dim3((unsigned)grid), dim3(kMaskThreads), 0u, stream,
                           ev.start, ev.stop, 0u, p);
   else

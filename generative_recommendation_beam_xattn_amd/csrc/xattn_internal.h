@@ -25,6 +25,14 @@ constexpr int kMaxTopkBeams = 512;
 // Largest beam width the Unshared-cache reorder takes.
 constexpr int kMaxReorderBeams = 2048;
 
+// Optional pair of events bound to kernel dispatches (hipExtLaunchKernel):
+// start is recorded as the dispatch begins and stop as it ends; a call of
+// several kernels binds start to its first and stop to its last.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Everything a decode launch needs; passed by value as a kernel argument.
 struct DecodeParams {
   const void *q;
@@ -36,6 +44,8 @@ struct DecodeParams {
   const int32_t *parent_idx;
   void *out;
   const int32_t *anc;  // [R][step+1][BW] resolved slots, or nullptr: walk in-kernel
+  float *tok_ml;       // deep chains: Unshared-stage partials per query row,
+  float *tok_o;        // (m, l) and unnormalised o [D], computed beforehand
   float *lse;          // optional taps (debug entry only)
   float *stage_ml;
   float *stage_o;
@@ -53,21 +63,20 @@ struct AncLayout {
   int64_t stride_r, stride_b, stride_t;
 };
 
-// Optional pair of events bound to one kernel dispatch (hipExtLaunchKernel):
-// start and stop then time that kernel alone.
-struct LaunchEvents {
-  hipEvent_t start = nullptr;
-  hipEvent_t stop = nullptr;
-};
 
 hipError_t launch_resolve_ancestors(const int32_t *parent_idx, int32_t R, int32_t BW, int32_t S,
                                     int32_t step, int32_t *anc, AncLayout layout,
-                                    hipStream_t stream);
+                                    hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream,
                               LaunchEvents ev = {});
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream,
                                        LaunchEvents ev = {});
+// Unshared stage alone for deep chains (p.anc resolved): per query row its
+// partial (m, l) into p.tok_ml and unnormalised o into p.tok_o, in the units
+// of the staged kernel's online softmax (raw scores, exp2 with scale_log2).
+hipError_t launch_token_partials_bf16(const DecodeParams &p, hipStream_t stream,
+                                      LaunchEvents ev = {});
 
 // In-place reorder of the Unshared cache: row (t, b) := old row (t, parent[b])
 // for t < n_levels, every request and KV head.

@@ -104,7 +104,10 @@ xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *s
 
 /* Bytes of device workspace xattn_decode / xattn_decode_debug need for this
  * shape and step (0 if none).  Returns (size_t)-1 if the shape or step is
- * invalid. */
+ * invalid.  Chains of more than 16 levels need it: the resolved ancestor
+ * slots, and for bf16 the Unshared stage's partial (m, l, o) of every query
+ * row, which a first kernel computes with one workgroup per (request, beam,
+ * KV head) before the attention kernel starts from them. */
 size_t xattn_workspace_size(const xattn_shape *shape, int32_t step);
 
 /*
@@ -142,10 +145,12 @@ xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const v
 /*
  * xattn_decode for measurement: identical work and results, and in addition
  * start_event / stop_event (hipEvent_t, created by the caller, both required)
- * are bound to the dispatch of the attention kernel itself, so
- * hipEventElapsedTime(start_event, stop_event) is that kernel's execution
- * time, with no queue or marker latency around it.  When the chain is deep
- * enough to need the ancestor kernel, that kernel runs before start_event.
+ * are bound to the kernel dispatches of the call -- start to the first
+ * kernel's, stop to the last one's -- so hipEventElapsedTime(start_event,
+ * stop_event) is the call's execution time on the device, with no queue or
+ * marker latency around it.  A call is one kernel, or for chains deeper than
+ * 16 levels up to three (ancestor slots, the Unshared stage for bf16, then
+ * attention).
  * Returns XATTN_EINVAL if an event is NULL.
  */
 xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const void *shared_k,

@@ -66,10 +66,14 @@ def shape(**kw):
 
 
 def test_workspace_size(lib):
+    up = lambda x: (x + 255) // 256 * 256
     assert B.workspace_size(shape(), 2) == 0
     s = shape(max_steps=40)
-    n = 2 * 40 * 4 * 4
-    assert B.workspace_size(s, 39) == (n + 255) // 256 * 256
+    n = 2 * 40 * 4 * 4                  # ancestor slots [R][step+1][BW] int32
+    rows = 2 * 4 * 8                    # query rows R * BW * Hq
+    # bf16: plus the Unshared-stage partials, (m, l) and o [D] per row, float
+    assert B.workspace_size(s, 39) == up(n) + up(rows * 2 * 4) + up(rows * 128 * 4)
+    assert B.workspace_size(shape(max_steps=40, dtype=B.XATTN_F32), 39) == up(n)
     assert B.workspace_size(s, 15) == 0
     assert B.workspace_size(s, 16) > 0
     assert lib.xattn_workspace_size(ctypes.byref(shape(num_requests=0)), 0) == ctypes.c_size_t(-1).value
