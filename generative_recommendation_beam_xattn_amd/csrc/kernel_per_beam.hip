@@ -48,8 +48,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPK, part = lane % LPK;
   const int sg = wave * KPW + sub;
-  const int k = blockIdx.x % p.Hkv;
-  const int b = (blockIdx.x / p.Hkv) % p.BW;
+  // per-beam comparison: KV head fastest, as a per-sequence grid orders it;
+  // the Unshared stage: beam fastest, so workgroups running side by side
+  // read neighbouring rows (t, b), (t, b + 1), ... of each level
+  const int k = TOKENS ? (blockIdx.x / p.BW) % p.Hkv : blockIdx.x % p.Hkv;
+  const int b = TOKENS ? blockIdx.x % p.BW : (blockIdx.x / p.Hkv) % p.BW;
   const int r = blockIdx.x / (p.Hkv * p.BW);
   const int step = p.step, BW = p.BW, G = p.G;
   const float c = p.scale_log2;
