@@ -137,6 +137,23 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
       : "memory");
 }
 
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the instruction's saddr form): no per-lane 64-bit address
+// arithmetic on the vector ALUs.
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, const void *lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(base)
+      : "memory");
+}
+
 // The same for 4 bytes per lane (global_load_lds_dword): lane i's 4 bytes
 // at src land at LDS byte address lds_base + 4 i.
 __device__ __forceinline__ void dma4(const void *src, const void *lds_dst) {
@@ -228,16 +245,15 @@ __device__ __forceinline__ void tile_copy(uint8_t *ktile, uint8_t *vtile,
     const bool is_v = qi >= C::NQ;
     const int q = is_v ? qi - C::NQ : qi;
     const uint8_t *base = reinterpret_cast<const uint8_t *>(is_v ? svg : skg);
-    const uint8_t *src;
+    uint8_t *dst = (is_v ? vtile : ktile) + q * 1024;
     if constexpr (!CLAMP) {
-      src = base + (int64_t)key0 * Gm::RB + cp.off[i];
+      // the tile's first row is uniform: only the lane's offset is per lane
+      dma16s(base + (int64_t)key0 * Gm::RB, cp.off[i], dst);
     } else {
       const int row = C::row_of(cp.off[i]);
       const int key = min(key0 + row, L - 1);
-      src = base + (int64_t)key * Gm::RB + (cp.off[i] - (uint32_t)(row * Gm::RB));
+      dma16(base + (int64_t)key * Gm::RB + (cp.off[i] - (uint32_t)(row * Gm::RB)), dst);
     }
-    uint8_t *dst = (is_v ? vtile : ktile) + q * 1024;
-    dma16(src, dst);
   }
 }
 
@@ -943,6 +959,11 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
               st.O[db][4 * j + 3] = v.w;
             }
         }
+        // the compiler counts these loads, not the tile copies issued before
+        // them: left pending, they would make it wait for vmcnt to reach 0 at
+        // their first use inside the tile loop, every iteration, draining the
+        // copy pipeline; completing them here clears that for the whole loop
+        wait_vm_lgkm0<0>();
       } else {
         TokenRows<D> none;
         unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step - kh, KSPLIT,
