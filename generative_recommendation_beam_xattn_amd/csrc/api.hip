@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/xattn.h"
 #include "../../include/xbeam.h"
 #include "xattn_internal.h"
@@ -65,12 +67,39 @@ size_t rows_of(const xattn_shape *s) {
   return (size_t)s->num_requests * (size_t)s->beam_width * (size_t)s->num_q_heads;
 }
 
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Key splits of a deep-chain bf16 call on the staged kernel: when its
+// (request, KV head, row block) workgroups cannot fill the GPU's 256
+// compute units, each one's prompt tiles are split over up to 4
+// workgroups (at least 4 tiles each), whose partials a merge kernel
+// combines.  A function of the shape alone, so that xattn_workspace_size
+// can count the partials.
+int key_splits_for(const xattn_shape *s, int32_t step) {
+  if (!deep_chain(step) || s->dtype != XATTN_BF16) return 1;
+  const int64_t M = (int64_t)s->beam_width * (s->num_q_heads / s->num_kv_heads);
+  if (M <= xattn::kPerBeamMaxRows) return 1;   // runs on the per-beam kernel
+  xattn::DecodeParams p{};
+  p.M = (int32_t)M;
+  const int64_t rows = xattn::bf16_rows_per_block(p);
+  const int64_t grid = (int64_t)s->num_requests * s->num_kv_heads * ((M + rows - 1) / rows);
+  if (grid >= 128) return 1;
+  const int64_t tiles = ((int64_t)s->max_prompt_len + 63) / 64;
+  const int64_t n = std::min<int64_t>({4, 256 / grid, tiles / 4});
+  return n >= 2 ? (int)n : 1;
+}
+
 size_t workspace_bytes_for(const xattn_shape *s, int32_t step) {
   if (!deep_chain(step)) return 0;
   size_t bytes = anc_bytes_for(s, step);
   if (s->dtype == XATTN_BF16) {
-    bytes += (rows_of(s) * 2 * sizeof(float) + 255) & ~size_t(255);
-    bytes += (rows_of(s) * (size_t)s->head_dim * sizeof(float) + 255) & ~size_t(255);
+    bytes += round256(rows_of(s) * 2 * sizeof(float));
+    bytes += round256(rows_of(s) * (size_t)s->head_dim * sizeof(float));
+    const size_t ns = (size_t)key_splits_for(s, step);
+    if (ns > 1) {
+      bytes += round256(ns * rows_of(s) * 2 * sizeof(float));
+      bytes += round256(ns * rows_of(s) * (size_t)s->head_dim * sizeof(float));
+    }
   }
   return bytes;
 }
@@ -129,6 +158,9 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   p.anc = nullptr;
   p.tok_ml = nullptr;
   p.tok_o = nullptr;
+  p.part_ml = nullptr;
+  p.part_o = nullptr;
+  p.n_split = 1;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
@@ -156,12 +188,21 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
     // spreads over the whole GPU; the staged kernel starts from its partials
     uint8_t *w = static_cast<uint8_t *>(workspace) + anc_bytes_for(s, step);
     p.tok_ml = reinterpret_cast<float *>(w);
-    p.tok_o = reinterpret_cast<float *>(w + ((rows_of(s) * 2 * sizeof(float) + 255) &
-                                             ~size_t(255)));
+    w += round256(rows_of(s) * 2 * sizeof(float));
+    p.tok_o = reinterpret_cast<float *>(w);
+    w += round256(rows_of(s) * (size_t)s->head_dim * sizeof(float));
+    const int ns = key_splits_for(s, step);
+    if (ns > 1) {
+      p.n_split = ns;
+      p.part_ml = reinterpret_cast<float *>(w);
+      w += round256((size_t)ns * rows_of(s) * 2 * sizeof(float));
+      p.part_o = reinterpret_cast<float *>(w);
+    }
     e = xattn::launch_token_partials_bf16(p, hs, first_ev());
     if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
   }
-  xattn::LaunchEvents ev_main = first ? ev : ev_last;
+  // with key splits the merge kernel is the call's last
+  xattn::LaunchEvents ev_main = p.n_split > 1 ? first_ev() : (first ? ev : ev_last);
   if (s->dtype == XATTN_F32)
     e = xattn::launch_decode_f32(p, hs, ev_main);  // per query row already: also the per-beam form
   else if (!staged_bf16)
@@ -169,6 +210,10 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   else
     e = xattn::launch_decode_bf16(p, taps, hs, ev_main);
   if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  if (p.n_split > 1) {
+    e = xattn::launch_merge_splits_bf16(p, hs, ev_last);
+    if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  }
   g_last_error[0] = '\0';
   return XATTN_OK;
 }

@@ -772,7 +772,8 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
 
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int rb = lb % p.n_rb;
-  const int unit = lb / p.n_rb;
+  const int split = (lb / p.n_rb) % p.n_split;   // key split (row blocks of one split adjacent)
+  const int unit = lb / p.n_rb / p.n_split;
   const int r = __builtin_amdgcn_readfirstlane(unit / p.Hkv);
   const int k = unit % p.Hkv;
   const int G = p.G, BW = p.BW, step = p.step;
@@ -837,21 +838,26 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
                         ((int64_t)r * p.Hkv + k) * p.Lmax * D;
   CopyPlan<D, WAVES> cplan;
   cplan.init(wave, lane);
-  const bool speculate = p.Lmax >= 3 * KT;
+  const bool speculate = p.n_split == 1 && p.Lmax >= 3 * KT;
   if (speculate) {
 #pragma unroll
     for (int i = 0; i < 3; ++i)
       tile_copy<D, WAVES, false>(tiles + i * Gm::TILE_BYTES, tiles + (NSTAGE + i) * Gm::TILE_BYTES,
                                  cplan, skg, svg, i * KT, 0, wave);
   }
-  const int n_tiles = (L + KT - 1) / KT;
-  // Tile t covers keys [t*KT, t*KT + KT); the last one's window is shifted
-  // back to [L - KT, L) (when L >= KT) so that no copy needs clamping; its
-  // keys below (n_tiles - 1) * KT were already counted and get masked.
+  // The prompt's tiles are split evenly over the key splits; this
+  // workgroup takes tiles [t_base, t_base + n_tiles) (its tile t is prompt
+  // tile t_base + t).
+  const int n_tiles_all = (L + KT - 1) / KT;
+  const int t_base = split * n_tiles_all / p.n_split;
+  const int n_tiles = (split + 1) * n_tiles_all / p.n_split - t_base;
+  // Prompt tile g covers keys [g*KT, g*KT + KT); the last one's window is
+  // shifted back to [L - KT, L) (when L >= KT) so that no copy needs
+  // clamping; its keys below g * KT were already counted and get masked.
   const int last_key0 = L >= KT ? L - KT : 0;
 #define XATTN_KT(S) (tiles + (S) * Gm::TILE_BYTES)
 #define XATTN_VT(S) (tiles + (NSTAGE + (S)) * Gm::TILE_BYTES)
-#define XATTN_KEY0(T) ((T) + 1 < n_tiles ? (T) * KT : last_key0)
+#define XATTN_KEY0(T) (t_base + (T) + 1 < n_tiles_all ? (t_base + (T)) * KT : last_key0)
   if (speculate && n_tiles > 3) {
     // the speculative copies are tiles 0, 1, 2
   } else if (L < KT) {
@@ -940,10 +946,10 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     if (!walk_here) {
       if (p.tok_o) {
         // the Unshared stage was computed beforehand, one workgroup per
-        // (request, beam, KV head): start from its partial; key half 1
-        // starts empty, and l lives in lane half 0 (the row total is the
-        // pair's sum)
-        if (kh == 0) {
+        // (request, beam, KV head): key split 0 starts from its partial;
+        // key half 1 starts empty, and l lives in lane half 0 (the row
+        // total is the pair's sum)
+        if (kh == 0 && split == 0) {
           const int64_t ro = qoff / D;
           st.m = p.tok_ml[ro * 2 + 0];
           st.l = hl == 0 ? p.tok_ml[ro * 2 + 1] : 0.f;
@@ -1037,7 +1043,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
 #undef XATTN_COPIED
   if (n_tiles > 0) {  // the last tile: every copy has landed
     const int t = n_tiles - 1;
-    const int lo = t * KT;            // keys below were counted by earlier tiles
+    const int lo = (t_base + t) * KT;   // keys below were counted by earlier tiles
     const int key0 = XATTN_KEY0(t);   // first key the tile holds
     const bool masked = key0 < lo || key0 + KT > L;
     const float mc = masked
@@ -1146,6 +1152,28 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // ---- Merge / epilogue
   const int64_t n_rows_all = (int64_t)p.R * BW * p.Hq;
   const int64_t ri = qoff / D;
+  if constexpr (!TAPS) {
+    if (p.n_split > 1) {
+      // one key split's partial (m, l, unnormalised O); merge_splits_kernel
+      // combines the splits and writes out
+      if (!valid) return;
+      const int64_t pr = split * n_rows_all + ri;
+      const float lt = pair_sum(st.l);
+      if (hl == 0) {
+        p.part_ml[pr * 2 + 0] = st.m;
+        p.part_ml[pr * 2 + 1] = lt;
+      }
+      float *po = p.part_o + pr * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4 *>(po + db * 32 + 8 * j + 4 * hl) =
+              make_float4(st.O[db][4 * j], st.O[db][4 * j + 1], st.O[db][4 * j + 2],
+                          st.O[db][4 * j + 3]);
+      return;
+    }
+  }
   if constexpr (TAPS) {
     // Shared partial (m, l, O) on its own; then the Unshared partial on its
     // own; then their explicit OnlineSoftmax merge.
@@ -1209,7 +1237,8 @@ hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream, LaunchEvents e
   constexpr int ROWS = RG * 32;
   DecodeParams p = p0;
   p.n_rb = (p.M + ROWS - 1) / ROWS;
-  const int64_t grid = (int64_t)p.R * p.Hkv * p.n_rb;
+  if (TAPS && p.n_split != 1) return hipErrorInvalidValue;
+  const int64_t grid = (int64_t)p.R * p.Hkv * p.n_rb * p.n_split;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   size_t dyn = 0;
   if (p.anc == nullptr) {
@@ -1246,9 +1275,58 @@ hipError_t launch_d(const DecodeParams &p, bool taps, hipStream_t stream, Launch
   return launch_cfg<D, 4, 2, false>(p, stream, ev);
 }
 
+// Merge of the key splits' partials (OnlineSoftmax over the splits, the
+// combine of the xGR summary's Merge stage applied to n_split partials):
+// one wave per query row, D / 64 dims per lane.  m = max_s m_s, weights
+// w_s = exp2((m_s - m) * scale_log2), out = sum_s w_s o_s / sum_s w_s l_s.
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t n_rows_all = (int64_t)p.R * p.BW * p.Hq;
+  const int64_t ri = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (ri >= n_rows_all) return;
+  const float c = p.scale_log2;
+  float m = -INFINITY;
+  for (int sp = 0; sp < p.n_split; ++sp) m = fmaxf(m, p.part_ml[(sp * n_rows_all + ri) * 2]);
+  float l = 0.f, acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  for (int sp = 0; sp < p.n_split; ++sp) {
+    const int64_t pr = sp * n_rows_all + ri;
+    const float ms = p.part_ml[pr * 2 + 0];
+    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ms - m) * c);
+    l += p.part_ml[pr * 2 + 1] * w;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] += p.part_o[pr * D + lane * PER + k] * w;
+  }
+  const float inv = 1.f / l;
+  uint16_t *op = static_cast<uint16_t *>(p.out) + ri * D + lane * PER;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const __bf16 v = (__bf16)(acc[k] * inv);
+    op[k] = *reinterpret_cast<const uint16_t *>(&v);
+  }
+  if (p.lse && lane == 0) p.lse[ri] = m * p.scale + __logf(l);
+}
+
 }  // namespace
 
 int bf16_rows_per_block(const DecodeParams &p) { return rows_per_block(p.M); }
+
+hipError_t launch_merge_splits_bf16(const DecodeParams &p, hipStream_t stream, LaunchEvents ev) {
+  const int64_t rows = (int64_t)p.R * p.BW * p.Hq;
+  const int64_t grid = (rows + 3) / 4;
+  if (grid > 0x7fffffff || p.n_split < 2) return hipErrorInvalidConfiguration;
+  auto kernel = p.D == 64 ? merge_splits_kernel<64> : merge_splits_kernel<128>;
+  if (p.D != 64 && p.D != 128) return hipErrorInvalidValue;
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0u, stream, ev.start, ev.stop,
+                          0u, p);
+  else
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream,
                               LaunchEvents ev) {

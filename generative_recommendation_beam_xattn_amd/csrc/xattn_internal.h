@@ -46,6 +46,8 @@ struct DecodeParams {
   const int32_t *anc;  // [R][step+1][BW] resolved slots, or nullptr: walk in-kernel
   float *tok_ml;       // deep chains: Unshared-stage partials per query row,
   float *tok_o;        // (m, l) and unnormalised o [D], computed beforehand
+  float *part_ml;      // key splits (n_split > 1): per split and query row the
+  float *part_o;       // partial (m, l) and unnormalised o [D], merged afterwards
   float *lse;          // optional taps (debug entry only)
   float *stage_ml;
   float *stage_o;
@@ -53,6 +55,7 @@ struct DecodeParams {
   int32_t G;           // Hq / Hkv, query heads per KV head
   int32_t M;           // BW * G query rows per (request, KV head)
   int32_t n_rb;        // row blocks per (request, KV head)
+  int32_t n_split;     // key splits of the prompt per row block (1: none)
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e): scores go through exp2
 };
@@ -136,5 +139,8 @@ int beam_topk_sample_len(int32_t BW, int32_t V);
 
 // Number of query rows one bf16 workgroup owns for this shape.
 int bf16_rows_per_block(const DecodeParams &p);
+// Key splits: combine p.n_split partials (p.part_ml, p.part_o) into p.out.
+hipError_t launch_merge_splits_bf16(const DecodeParams &p, hipStream_t stream,
+                                    LaunchEvents ev = {});
 
 }  // namespace xattn

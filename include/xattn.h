@@ -107,7 +107,11 @@ xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *s
  * invalid.  Chains of more than 16 levels need it: the resolved ancestor
  * slots, and for bf16 the Unshared stage's partial (m, l, o) of every query
  * row, which a first kernel computes with one workgroup per (request, beam,
- * KV head) before the attention kernel starts from them. */
+ * KV head) before the attention kernel starts from them.  When such a bf16
+ * call has fewer than 128 (request, KV head, row block) workgroups and
+ * a prompt of at least 8 tiles of 64 keys, each workgroup's prompt tiles
+ * are split over up to 4 workgroups; the workspace then also holds every
+ * split's partial (m, l, o) per query row, which a last kernel merges. */
 size_t xattn_workspace_size(const xattn_shape *shape, int32_t step);
 
 /*

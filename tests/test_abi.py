@@ -75,6 +75,16 @@ def test_workspace_size(lib):
     assert B.workspace_size(s, 39) == up(n) + up(rows * 2 * 4) + up(rows * 128 * 4)
     assert B.workspace_size(shape(max_steps=40, dtype=B.XATTN_F32), 39) == up(n)
     assert B.workspace_size(s, 15) == 0
+    # few (request, KV head, row block) workgroups and a long prompt: the
+    # prompt tiles are split over 4 workgroups, whose partials (m, l) and o
+    # [D] per query row are kept for the merge
+    s2 = shape(num_requests=1, beam_width=32, max_prompt_len=1024, max_steps=40)
+    n2, rows2 = 1 * 40 * 32 * 4, 32 * 8
+    base2 = up(n2) + up(rows2 * 2 * 4) + up(rows2 * 128 * 4)
+    assert B.workspace_size(s2, 39) == base2 + up(4 * rows2 * 2 * 4) + up(4 * rows2 * 128 * 4)
+    # a prompt of fewer than 8 tiles is not split
+    s3 = shape(num_requests=1, beam_width=32, max_prompt_len=448, max_steps=40)
+    assert B.workspace_size(s3, 39) == base2
     assert B.workspace_size(s, 16) > 0
     assert lib.xattn_workspace_size(ctypes.byref(shape(num_requests=0)), 0) == ctypes.c_size_t(-1).value
     assert lib.xattn_workspace_size(None, 0) == ctypes.c_size_t(-1).value

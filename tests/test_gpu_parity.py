@@ -46,6 +46,12 @@ SMALL = {
     "qb2_tiling": dict(R=64, BW=64, Hq=32, Hkv=8, D=128, L=(30, 150), steps=[1], S=2),
     "deep_chain_workspace": dict(R=2, BW=6, Hq=4, Hkv=2, D=128, L=[50, 0], steps=[39], S=40),
     "deep_chain_wide": dict(R=1, BW=300, Hq=4, Hkv=4, D=64, L=[65], steps=[20], S=24),
+    # deep chains whose few workgroups split their prompt tiles: 4 splits
+    # (the short request leaves split 0 without a tile and masks a ragged
+    # tail), and 2 splits at head_dim 64
+    "deep_key_splits_ragged": dict(R=2, BW=32, Hq=8, Hkv=2, D=128, L=[1000, 130], steps=[20],
+                                   S=21),
+    "deep_key_splits_d64": dict(R=1, BW=16, Hq=8, Hkv=1, D=64, L=[700], steps=[17], S=18),
     "single_beam_empty_prompt": dict(R=2, BW=1, Hq=4, Hkv=1, D=128, L=[0, 0], steps=[0]),
     "no_shared_rows": dict(R=2, BW=3, Hq=4, Hkv=2, D=64, L=[0, 0], steps=[1], Lmax=0),
     # either side of the row count below which bf16 calls go to the per-beam
