@@ -33,6 +33,31 @@ constexpr int kKeysInFlight = 4;  // keys per lane group whose loads go out toge
 __device__ inline float lo_f(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ inline float hi_f(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// x from another lane of the same 16-lane DPP row, by DPP control `ctrl`.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over an aligned group of LPK (8 or 16) lanes, returned to every lane
+// of the group, on the vector ALUs: pairs (quad_perm 1,0,3,2), quads
+// (quad_perm 2,3,0,1), half rows (row_half_mirror), rows (row_mirror).
+template <int LPK>
+__device__ __forceinline__ float group_sum(float s) {
+  static_assert(LPK == 8 || LPK == 16, "a lane group is half or all of a DPP row");
+  s += dpp_f<0xB1>(s);
+  s += dpp_f<0x4E>(s);
+  s += dpp_f<0x141>(s);
+  if constexpr (LPK == 16) s += dpp_f<0x140>(s);
+  return s;
+}
+
+// A lane group's running maximum only moves when a score exceeds it by
+// more than 2^8 in the exp2 domain; until then exp2(s - m) may exceed 1 (by
+// at most 256), which the fp32 sums hold without loss of range.
+constexpr float kLazyRescaleLog2 = 8.0f;
+
 // TOKENS: the Unshared stage alone (keys = the beam's tokens at levels
 // 0..step), written as an online-softmax partial for the staged kernel to
 // start from, instead of normalised output.
@@ -56,6 +81,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
   const int r = blockIdx.x / (p.Hkv * p.BW);
   const int step = p.step, BW = p.BW, G = p.G;
   const float c = p.scale_log2;
+  const float thr = kLazyRescaleLog2 / c;   // in raw dot-product units
 
   // the beam's ancestor slot at every level: walked here for short chains,
   // resolved into the workspace beforehand for deep ones
@@ -135,31 +161,69 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
         kvu[u] = *reinterpret_cast<const uint4 *>(kr + part * 8);
         vvu[u] = *reinterpret_cast<const uint4 *>(vr + part * 8);
       }
+      // scores of the keys in flight against the pass's query rows (a key
+      // past the end scores -inf and adds nothing)
+      float sc[kKeysInFlight][kRowsPerPass];
 #pragma unroll
       for (int u = 0; u < kKeysInFlight; ++u) {
-        if (i0 + u * NSG >= n_keys) break;   // the lane group's keys are done
         const uint32_t kw[4] = {kvu[u].x, kvu[u].y, kvu[u].z, kvu[u].w};
-        const uint32_t vw[4] = {vvu[u].x, vvu[u].y, vvu[u].z, vvu[u].w};
 #pragma unroll
         for (int j = 0; j < kRowsPerPass; ++j) {
           const uint32_t qw[4] = {qv[j].x, qv[j].y, qv[j].z, qv[j].w};
-          float s = 0.f;
+          float x = 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[e]),
-                                                __builtin_bit_cast(bf16x2, kw[e]), s, false);
+            x = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[e]),
+                                                __builtin_bit_cast(bf16x2, kw[e]), x, false);
+          x = group_sum<LPK>(x);
+          sc[u][j] = i0 + u * NSG < n_keys ? x : -INFINITY;
+        }
+      }
+      // online softmax of this lane group's keys (scores in exp2 units).
+      // The maximum is raised lazily and rarely: then the keys are taken
+      // one by one with the full update; otherwise they add exp2(s - m).
+      bool raise = false;
 #pragma unroll
-          for (int w = LPK / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, LPK);
-          // online softmax of this lane group's keys (scores in exp2 units)
-          const float mn = fmaxf(m[j], s);
-          const float alpha = __builtin_amdgcn_exp2f((m[j] - mn) * c);   // 0 while m is -inf
-          const float pr = __builtin_amdgcn_exp2f((s - mn) * c);
-          m[j] = mn;
-          l[j] = l[j] * alpha + pr;
+      for (int u = 0; u < kKeysInFlight; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[j][2 * e] = fmaf(o[j][2 * e], alpha, pr * lo_f(vw[e]));
-            o[j][2 * e + 1] = fmaf(o[j][2 * e + 1], alpha, pr * hi_f(vw[e]));
+        for (int j = 0; j < kRowsPerPass; ++j) raise |= sc[u][j] > m[j] + thr;
+      if (__any(raise)) {
+#pragma unroll
+        for (int u = 0; u < kKeysInFlight; ++u) {
+          const uint32_t vw[4] = {vvu[u].x, vvu[u].y, vvu[u].z, vvu[u].w};
+#pragma unroll
+          for (int j = 0; j < kRowsPerPass; ++j) {
+            const float x = sc[u][j];
+            if (x > m[j] + thr) {
+              const float mn = fmaxf(m[j], x);
+              const float alpha = __builtin_amdgcn_exp2f((m[j] - mn) * c);   // 0 while m is -inf
+              m[j] = mn;
+              l[j] *= alpha;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) o[j][e] *= alpha;
+            }
+            const float pr = __builtin_amdgcn_exp2f((x - m[j]) * c);
+            l[j] += pr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[j][2 * e] = fmaf(pr, lo_f(vw[e]), o[j][2 * e]);
+              o[j][2 * e + 1] = fmaf(pr, hi_f(vw[e]), o[j][2 * e + 1]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kKeysInFlight; ++u) {
+          const uint32_t vw[4] = {vvu[u].x, vvu[u].y, vvu[u].z, vvu[u].w};
+#pragma unroll
+          for (int j = 0; j < kRowsPerPass; ++j) {
+            const float pr = __builtin_amdgcn_exp2f((sc[u][j] - m[j]) * c);
+            l[j] += pr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[j][2 * e] = fmaf(pr, lo_f(vw[e]), o[j][2 * e]);
+              o[j][2 * e + 1] = fmaf(pr, hi_f(vw[e]), o[j][2 * e + 1]);
+            }
           }
         }
       }
