@@ -56,10 +56,20 @@ xattn_status check_shape(const xattn_shape *s, int32_t step) {
 
 bool deep_chain(int32_t step) { return step + 1 > xattn::kMaxInKernelLevels; }
 
-// Workspace of a deep-chain call: the resolved ancestor slots, then (bf16)
-// the Unshared-stage partials of every query row, (m, l) and o [D] in float.
+// Workspace of a deep-chain call: the resolved ancestor slots, the composed
+// parent maps of the segmented walk (long chains), then (bf16) the
+// Unshared-stage partials of every query row, (m, l) and o [D] in float,
+// and the key splits' partials.
 size_t anc_bytes_for(const xattn_shape *s, int32_t step) {
   const size_t n = (size_t)s->num_requests * (size_t)(step + 1) * (size_t)s->beam_width;
+  return (n * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
+size_t seg_map_bytes_for(const xattn_shape *s, int32_t step) {
+  const int lps = xattn::ancestor_segment_levels(s->beam_width, step);
+  if (lps == 0) return 0;
+  const size_t n = (size_t)s->num_requests * (size_t)((step + lps - 1) / lps) *
+                   (size_t)s->beam_width;
   return (n * sizeof(int32_t) + 255) & ~size_t(255);
 }
 
@@ -91,7 +101,7 @@ int key_splits_for(const xattn_shape *s, int32_t step) {
 
 size_t workspace_bytes_for(const xattn_shape *s, int32_t step) {
   if (!deep_chain(step)) return 0;
-  size_t bytes = anc_bytes_for(s, step);
+  size_t bytes = anc_bytes_for(s, step) + seg_map_bytes_for(s, step);
   if (s->dtype == XATTN_BF16) {
     bytes += round256(rows_of(s) * 2 * sizeof(float));
     bytes += round256(rows_of(s) * (size_t)s->head_dim * sizeof(float));
@@ -175,8 +185,17 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   if (need > 0) {
     int32_t *anc = static_cast<int32_t *>(workspace);
     const xattn::AncLayout lay{(int64_t)(step + 1) * p.BW, 1, p.BW};  // [R][step+1][BW]
-    e = xattn::launch_resolve_ancestors(parent_idx, p.R, p.BW, p.S, step, anc, lay, hs,
-                                        first_ev());
+    if (seg_map_bytes_for(s, step) > 0) {
+      int32_t *fmap = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) +
+                                                  anc_bytes_for(s, step));
+      // both walk kernels go in the call's timing window
+      xattn::LaunchEvents ev_walk = first_ev();
+      e = xattn::launch_resolve_ancestors_segmented(parent_idx, p.R, p.BW, p.S, step, anc, lay,
+                                                    fmap, hs, ev_walk);
+    } else {
+      e = xattn::launch_resolve_ancestors(parent_idx, p.R, p.BW, p.S, step, anc, lay, hs,
+                                          first_ev());
+    }
     if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
     p.anc = anc;
   }
@@ -186,7 +205,8 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
     // deep chains: the Unshared stage runs first with one workgroup per
     // (request, beam, KV head), so the gather of every beam's token rows
     // spreads over the whole GPU; the staged kernel starts from its partials
-    uint8_t *w = static_cast<uint8_t *>(workspace) + anc_bytes_for(s, step);
+    uint8_t *w = static_cast<uint8_t *>(workspace) + anc_bytes_for(s, step) +
+                 seg_map_bytes_for(s, step);
     p.tok_ml = reinterpret_cast<float *>(w);
     w += round256(rows_of(s) * 2 * sizeof(float));
     p.tok_o = reinterpret_cast<float *>(w);

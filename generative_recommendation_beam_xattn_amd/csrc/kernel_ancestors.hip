@@ -11,7 +11,18 @@
 // round trip), the next chunk's rows are already being loaded -- into
 // registers, every load of the chunk in flight at once -- and stored to
 // the other buffer after the walk.
+//
+// Long chains split the levels into segments walked side by side.  A first
+// kernel composes each segment's parent maps: for every slot x at the
+// segment's top level, the slot reached at the level below its bottom.  A
+// second kernel gives each segment the entry slot of every beam -- the
+// beam's slot pushed through the composed maps of the segments above --
+// and walks the segment from there, writing the ancestor slots.  The
+// dependent chain per beam shrinks from one step per level to one per
+// level of a segment plus one per segment.
 #include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "xattn_internal.h"
 
@@ -21,6 +32,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kLdsInts = 8192;               // per buffer: 32 KiB of parent rows
 constexpr int kPerThread = kLdsInts / kThreads;
+constexpr int kSegMapInts = 16384;           // composed maps of the segments above: 64 KiB
 
 template <bool kStaged>
 __global__ __launch_bounds__(kThreads) void resolve_ancestors_kernel(
@@ -81,7 +93,111 @@ __global__ __launch_bounds__(kThreads) void resolve_ancestors_kernel(
   }
 }
 
+// n consecutive int32 from global memory into LDS, eight loads per thread
+// in flight at a time.
+__device__ inline void copy_to_lds(const int32_t *src, int n, int32_t *dst) {
+  constexpr int kBatch = 8;
+  for (int base = 0; base < n; base += kBatch * kThreads) {
+    int32_t v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + u * kThreads + threadIdx.x;
+      v[u] = i < n ? src[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + u * kThreads + threadIdx.x;
+      if (i < n) dst[i] = v[u];
+    }
+  }
+}
+
+// Segment j covers parent levels hi_j = step - j * lps down to
+// lo_j = max(1, hi_j - lps + 1); its rows are staged in LDS ascending.
+__device__ inline void segment_rows(const int32_t *par, int32_t BW, int hi, int lo,
+                                    int32_t *rows) {
+  copy_to_lds(par + (int64_t)lo * BW, (hi - lo + 1) * BW, rows);
+}
+
+// LDS of both segment kernels (dynamic, sized to the shape): the segment's
+// parent rows, lps * BW int32, then (walk) the composed maps of the
+// segments above, up to (n_seg - 1) * BW int32.
+__global__ __launch_bounds__(kThreads) void ancestor_segments_kernel(
+    const int32_t *__restrict__ parent_idx, int32_t BW, int32_t S, int32_t step, int32_t lps,
+    int32_t n_seg, int32_t *__restrict__ fmap) {
+  extern __shared__ int32_t seg_lds[];
+  int32_t *rows = seg_lds;
+  const int r = blockIdx.x / n_seg, j = blockIdx.x % n_seg;
+  const int hi = step - j * lps, lo = max(1, hi - lps + 1);
+  segment_rows(parent_idx + (int64_t)r * S * BW, BW, hi, lo, rows);
+  __syncthreads();
+  int32_t *f = fmap + ((int64_t)r * n_seg + j) * BW;
+  for (int x = threadIdx.x; x < BW; x += kThreads) {
+    int a = x;
+    for (int t = hi; t >= lo; --t) a = min(max(rows[(t - lo) * BW + a], 0), BW - 1);
+    f[x] = a;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void ancestor_segment_walk_kernel(
+    const int32_t *__restrict__ parent_idx, int32_t BW, int32_t S, int32_t step, int32_t lps,
+    int32_t n_seg, const int32_t *__restrict__ fmap, int32_t *__restrict__ anc, AncLayout lay) {
+  extern __shared__ int32_t seg_lds[];
+  int32_t *rows = seg_lds, *maps = seg_lds + lps * BW;
+  const int r = blockIdx.x / n_seg, j = blockIdx.x % n_seg;
+  const int hi = step - j * lps, lo = max(1, hi - lps + 1);
+  segment_rows(parent_idx + (int64_t)r * S * BW, BW, hi, lo, rows);
+  copy_to_lds(fmap + (int64_t)r * n_seg * BW, j * BW, maps);
+  __syncthreads();
+  for (int b = threadIdx.x; b < BW; b += kThreads) {
+    int32_t *dst = anc + r * lay.stride_r + (int64_t)b * lay.stride_b;
+    int a = b;
+    for (int i = 0; i < j; ++i) a = maps[i * BW + a];   // the beam's slot at level hi
+    if (j == 0) dst[(int64_t)step * lay.stride_t] = a;
+    for (int t = hi; t >= lo; --t) {
+      a = min(max(rows[(t - lo) * BW + a], 0), BW - 1);
+      dst[(int64_t)(t - 1) * lay.stride_t] = a;
+    }
+  }
+}
+
 }  // namespace
+
+int ancestor_segment_levels(int32_t BW, int32_t step) {
+  if (BW < 1 || step < 1 || BW > kLdsInts / 8) return 0;
+  const int lps = std::min(64, kLdsInts / BW);
+  const int64_t n_seg = (step + lps - 1) / lps;
+  if (n_seg < 2 || n_seg * BW > kSegMapInts) return 0;
+  return lps;
+}
+
+hipError_t launch_resolve_ancestors_segmented(const int32_t *parent_idx, int32_t R, int32_t BW,
+                                              int32_t S, int32_t step, int32_t *anc,
+                                              AncLayout layout, int32_t *fmap,
+                                              hipStream_t stream, LaunchEvents ev) {
+  const int lps = ancestor_segment_levels(BW, step);
+  if (lps == 0) return hipErrorInvalidValue;
+  const int32_t n_seg = (step + lps - 1) / lps;
+  const int64_t grid = (int64_t)R * n_seg;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const uint32_t lds_rows = (uint32_t)(lps * BW) * sizeof(int32_t);
+  const uint32_t lds_walk = lds_rows + (uint32_t)((n_seg - 1) * BW) * sizeof(int32_t);
+  if (ev.start)
+    hipExtLaunchKernelGGL(ancestor_segments_kernel, dim3((unsigned)grid), dim3(kThreads), lds_rows,
+                          stream, ev.start, nullptr, 0u, parent_idx, BW, S, step, lps, n_seg,
+                          fmap);
+  else
+    hipLaunchKernelGGL(ancestor_segments_kernel, dim3((unsigned)grid), dim3(kThreads), lds_rows,
+                       stream, parent_idx, BW, S, step, lps, n_seg, fmap);
+  if (ev.stop)
+    hipExtLaunchKernelGGL(ancestor_segment_walk_kernel, dim3((unsigned)grid), dim3(kThreads),
+                          lds_walk, stream, nullptr, ev.stop, 0u, parent_idx, BW, S, step, lps,
+                          n_seg, fmap, anc, layout);
+  else
+    hipLaunchKernelGGL(ancestor_segment_walk_kernel, dim3((unsigned)grid), dim3(kThreads),
+                       lds_walk, stream, parent_idx, BW, S, step, lps, n_seg, fmap, anc, layout);
+  return hipGetLastError();
+}
 
 hipError_t launch_resolve_ancestors(const int32_t *parent_idx, int32_t R, int32_t BW, int32_t S,
                                     int32_t step, int32_t *anc, AncLayout layout,

@@ -70,6 +70,14 @@ struct AncLayout {
 hipError_t launch_resolve_ancestors(const int32_t *parent_idx, int32_t R, int32_t BW, int32_t S,
                                     int32_t step, int32_t *anc, AncLayout layout,
                                     hipStream_t stream, LaunchEvents ev = {});
+// Long chains: levels per segment of the two-kernel segmented walk, or 0
+// when it does not apply (one segment, or too many slots for LDS).  fmap
+// holds R * ceil(step / levels) * BW int32 of composed segment maps.
+int ancestor_segment_levels(int32_t BW, int32_t step);
+hipError_t launch_resolve_ancestors_segmented(const int32_t *parent_idx, int32_t R, int32_t BW,
+                                              int32_t S, int32_t step, int32_t *anc,
+                                              AncLayout layout, int32_t *fmap,
+                                              hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stream,
                               LaunchEvents ev = {});
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev = {});

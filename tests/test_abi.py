@@ -85,6 +85,12 @@ def test_workspace_size(lib):
     # a prompt of fewer than 8 tiles is not split
     s3 = shape(num_requests=1, beam_width=32, max_prompt_len=448, max_steps=40)
     assert B.workspace_size(s3, 39) == base2
+    # chains longer than one walk segment (64 levels for 40 beams) keep the
+    # composed parent map of each segment, [R][segments][BW] int32
+    s4 = shape(num_requests=2, beam_width=40, max_steps=151)
+    rows4 = 2 * 40 * 8
+    assert B.workspace_size(s4, 150) == (up(2 * 151 * 40 * 4) + up(2 * 3 * 40 * 4) +
+                                         up(rows4 * 2 * 4) + up(rows4 * 128 * 4))
     assert B.workspace_size(s, 16) > 0
     assert lib.xattn_workspace_size(ctypes.byref(shape(num_requests=0)), 0) == ctypes.c_size_t(-1).value
     assert lib.xattn_workspace_size(None, 0) == ctypes.c_size_t(-1).value

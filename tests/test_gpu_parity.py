@@ -52,6 +52,11 @@ SMALL = {
     "deep_key_splits_ragged": dict(R=2, BW=32, Hq=8, Hkv=2, D=128, L=[1000, 130], steps=[20],
                                    S=21),
     "deep_key_splits_d64": dict(R=1, BW=16, Hq=8, Hkv=1, D=64, L=[700], steps=[17], S=18),
+    # chains long enough for the segmented ancestor walk: 3 segments of 64
+    # levels, and 4 segments of 27 levels with more beams than threads
+    "deep_segmented_walk": dict(R=2, BW=40, Hq=4, Hkv=2, D=128, L=[100, 20], steps=[150],
+                                S=151),
+    "deep_segmented_wide": dict(R=1, BW=300, Hq=2, Hkv=2, D=64, L=[40], steps=[100], S=101),
     "single_beam_empty_prompt": dict(R=2, BW=1, Hq=4, Hkv=1, D=128, L=[0, 0], steps=[0]),
     "no_shared_rows": dict(R=2, BW=3, Hq=4, Hkv=2, D=64, L=[0, 0], steps=[1], Lmax=0),
     # either side of the row count below which bf16 calls go to the per-beam
