@@ -95,7 +95,7 @@ int key_splits_for(const xattn_shape *s, int32_t step) {
   const int64_t grid = (int64_t)s->num_requests * s->num_kv_heads * ((M + rows - 1) / rows);
   if (grid >= 128) return 1;
   const int64_t tiles = ((int64_t)s->max_prompt_len + 63) / 64;
-  const int64_t n = std::min<int64_t>({4, 256 / grid, tiles / 4});
+  const int64_t n = std::min<int64_t>({xattn::kMaxKeySplits, 256 / grid, tiles / 4});
   return n >= 2 ? (int)n : 1;
 }
 

@@ -1287,18 +1287,30 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p) {
   const int64_t ri = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (ri >= n_rows_all) return;
   const float c = p.scale_log2;
+  // every split's (m, l) and o loads go out together
+  float ms[kMaxKeySplits], ls[kMaxKeySplits], os[kMaxKeySplits][PER];
+#pragma unroll
+  for (int sp = 0; sp < kMaxKeySplits; ++sp) {
+    const bool in = sp < p.n_split;
+    const int64_t pr = (in ? sp : 0) * n_rows_all + ri;
+    const float2 ml = *reinterpret_cast<const float2 *>(p.part_ml + pr * 2);
+    ms[sp] = in ? ml.x : -INFINITY;
+    ls[sp] = in ? ml.y : 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) os[sp][k] = in ? p.part_o[pr * D + lane * PER + k] : 0.f;
+  }
   float m = -INFINITY;
-  for (int sp = 0; sp < p.n_split; ++sp) m = fmaxf(m, p.part_ml[(sp * n_rows_all + ri) * 2]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxKeySplits; ++sp) m = fmaxf(m, ms[sp]);
   float l = 0.f, acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  for (int sp = 0; sp < p.n_split; ++sp) {
-    const int64_t pr = sp * n_rows_all + ri;
-    const float ms = p.part_ml[pr * 2 + 0];
-    const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ms - m) * c);
-    l += p.part_ml[pr * 2 + 1] * w;
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] += p.part_o[pr * D + lane * PER + k] * w;
+  for (int sp = 0; sp < kMaxKeySplits; ++sp) {
+    const float w = ms[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((ms[sp] - m) * c);
+    l += ls[sp] * w;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] += os[sp][k] * w;
   }
   const float inv = 1.f / l;
   uint16_t *op = static_cast<uint16_t *>(p.out) + ri * D + lane * PER;
@@ -1317,7 +1329,8 @@ int bf16_rows_per_block(const DecodeParams &p) { return rows_per_block(p.M); }
 hipError_t launch_merge_splits_bf16(const DecodeParams &p, hipStream_t stream, LaunchEvents ev) {
   const int64_t rows = (int64_t)p.R * p.BW * p.Hq;
   const int64_t grid = (rows + 3) / 4;
-  if (grid > 0x7fffffff || p.n_split < 2) return hipErrorInvalidConfiguration;
+  if (grid > 0x7fffffff || p.n_split < 2 || p.n_split > kMaxKeySplits)
+    return hipErrorInvalidConfiguration;
   auto kernel = p.D == 64 ? merge_splits_kernel<64> : merge_splits_kernel<128>;
   if (p.D != 64 && p.D != 128) return hipErrorInvalidValue;
   if (ev.start || ev.stop)

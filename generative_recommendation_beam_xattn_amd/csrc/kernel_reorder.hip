@@ -9,12 +9,13 @@
 //
 // Hazards.  A row may be the source of several beams and the destination of
 // another, so rows cannot be moved one by one.  One workgroup owns one
-// (request, KV head, level) slice -- all BW rows of it -- and stages the
-// whole slice (in column chunks that fit LDS) before writing any of it: all
-// reads of a chunk precede all writes of that chunk, behind a barrier, and
-// no other workgroup touches the slice.  Rows whose parent is themselves are
-// not rewritten, and a slice whose parents are all the identity is left
-// untouched without a read.
+// column chunk of K or of V of one (request, KV head, level) slice -- that
+// chunk of all BW rows -- and stages it whole in LDS before writing any of
+// it: all reads precede all writes, behind a barrier, and no other
+// workgroup touches those bytes.  Splitting the slice by K/V and columns
+// spreads a level's few slices over many workgroups.  Rows whose parent is
+// themselves are not rewritten, and a slice whose parents are all the
+// identity is left untouched without a read.
 #include <hip/hip_ext.h>
 
 #include "xattn_internal.h"
@@ -31,8 +32,11 @@ __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParam
   extern __shared__ int32_t par[];   // BW parent slots (dynamic)
 
   const int tid = threadIdx.x;
-  const int t = blockIdx.x % p.n_levels;
-  const int rk = blockIdx.x / p.n_levels;
+  const int n_cc = (int)(p.row_bytes / p.chunk_bytes);   // column chunks per row
+  const int part = blockIdx.x % (2 * n_cc);               // K chunks, then V chunks
+  const int slice_id = blockIdx.x / (2 * n_cc);
+  const int t = slice_id % p.n_levels;
+  const int rk = slice_id / p.n_levels;
   const int k = rk % p.Hkv;
   const int r = rk / p.Hkv;
   const int BW = p.BW;
@@ -53,33 +57,31 @@ __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParam
   const int64_t slice = (((int64_t)r * p.Hkv + k) * p.S + t) * BW * RB;
   const int units_per_row = (int)(p.chunk_bytes / 16);    // 16-byte units per row per chunk
   const int n_units = BW * units_per_row;
-  for (int which = 0; which < 2; ++which) {
-    uint8_t *base = static_cast<uint8_t *>(which == 0 ? p.unshared_k : p.unshared_v) + slice;
-    for (int64_t c0 = 0; c0 < RB; c0 += p.chunk_bytes) {
-      // stage columns [c0, c0 + chunk) of every row of the slice
-      for (int u = tid; u < n_units; u += kThreads) {
-        const int b = u / units_per_row, c = u - b * units_per_row;
-        *reinterpret_cast<uint4 *>(stage + (int64_t)u * 16) =
-            *reinterpret_cast<const uint4 *>(base + (int64_t)b * RB + c0 + c * 16);
-      }
-      __syncthreads();
-      // every read of this chunk is done: write the moved rows
-      for (int u = tid; u < n_units; u += kThreads) {
-        const int b = u / units_per_row, c = u - b * units_per_row;
-        const int a = par[b];
-        if (a != b)
-          *reinterpret_cast<uint4 *>(base + (int64_t)b * RB + c0 + c * 16) =
-              *reinterpret_cast<const uint4 *>(stage + ((int64_t)a * units_per_row + c) * 16);
-      }
-      __syncthreads();
-    }
+  uint8_t *base = static_cast<uint8_t *>(part < n_cc ? p.unshared_k : p.unshared_v) + slice;
+  const int64_t c0 = (int64_t)(part % n_cc) * p.chunk_bytes;
+  // stage columns [c0, c0 + chunk) of every row of the slice
+  for (int u = tid; u < n_units; u += kThreads) {
+    const int b = u / units_per_row, c = u - b * units_per_row;
+    *reinterpret_cast<uint4 *>(stage + (int64_t)u * 16) =
+        *reinterpret_cast<const uint4 *>(base + (int64_t)b * RB + c0 + c * 16);
+  }
+  __syncthreads();
+  // every read of this chunk is done: write the moved rows
+  for (int u = tid; u < n_units; u += kThreads) {
+    const int b = u / units_per_row, c = u - b * units_per_row;
+    const int a = par[b];
+    if (a != b)
+      *reinterpret_cast<uint4 *>(base + (int64_t)b * RB + c0 + c * 16) =
+          *reinterpret_cast<const uint4 *>(stage + ((int64_t)a * units_per_row + c) * 16);
   }
 }
 
 }  // namespace
 
 hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, LaunchEvents ev) {
-  const int64_t grid = (int64_t)p.R * p.Hkv * p.n_levels;
+  if (p.chunk_bytes <= 0) return hipErrorInvalidConfiguration;
+  // per slice: K and V, each in row_bytes / chunk_bytes column chunks
+  const int64_t grid = (int64_t)p.R * p.Hkv * p.n_levels * 2 * (p.row_bytes / p.chunk_bytes);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff || p.BW > kMaxReorderBeams || p.chunk_bytes <= 0 ||
       (int64_t)p.BW * p.chunk_bytes > kStageBytes || p.chunk_bytes % 16 != 0 ||
@@ -95,9 +97,10 @@ hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, L
 }
 
 int64_t reorder_chunk_bytes(int64_t row_bytes, int32_t BW) {
-  // the largest power-of-two divisor of the row that lets BW rows fit LDS
+  // the largest power-of-two divisor of the row that lets BW rows fit LDS,
+  // and at most 64 bytes: more, smaller workgroups per slice
   int64_t c = row_bytes;
-  while (c > 16 && (int64_t)BW * c > kStageBytes) c /= 2;
+  while (c > 16 && ((int64_t)BW * c > kStageBytes || c > 64)) c /= 2;
   return c;
 }
 

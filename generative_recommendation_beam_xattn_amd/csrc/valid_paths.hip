@@ -14,8 +14,8 @@
 // out in one caller-provided host buffer; the caller copies it to the device.
 //
 // Kernels.  valid_mask_kernel masks one logits row per workgroup in place:
-// the row's bitmap is the node's dense bit row (early depths) or is built in
-// LDS from the node's children (later depths), and only invalid entries are
+// the row's bitmap, in LDS, is the node's dense bit row (early depths) or is
+// built from the node's children (later depths), and only invalid entries are
 // written (-inf); valid ones are not touched.  trie_advance_kernel moves
 // every new beam to the child of its parent's node through its new token
 // (-1 when the path leaves the vocabulary).
@@ -53,7 +53,13 @@ __global__ __launch_bounds__(kMaskThreads) void valid_mask_kernel(MaskParams p) 
     __syncthreads();
     mrow = bits;
   } else if (p.dense) {
-    mrow = reinterpret_cast<const uint32_t *>(p.table + p.mask_off) + (int64_t)n * words;
+    // the node's dense row into LDS with one coalesced load per thread, so
+    // the groups below test bits without a global round trip each
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(p.table + p.mask_off) +
+                          (int64_t)n * words;
+    for (int w = tid; w < words; w += kMaskThreads) bits[w] = src[w];
+    __syncthreads();
+    mrow = bits;
   } else {
     for (int w = tid; w < words; w += kMaskThreads) bits[w] = 0u;
     __syncthreads();

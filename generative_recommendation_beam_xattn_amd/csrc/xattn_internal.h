@@ -19,6 +19,8 @@ constexpr int kMaxInKernelLevels = 16;
 // prefix-sharing shapes: 1079 vs 2903 us at 4 rows, 957 vs 1498 us at 8,
 // and the staged kernel ahead from 16 rows).
 constexpr int kPerBeamMaxRows = 8;
+// Most key splits one staged workgroup's prompt tiles are spread over.
+constexpr int kMaxKeySplits = 4;
 
 // Largest beam width the beam-selection kernel takes.
 constexpr int kMaxTopkBeams = 512;
