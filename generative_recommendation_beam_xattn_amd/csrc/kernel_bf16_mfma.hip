@@ -1123,7 +1123,13 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       xs[64 + lane] = st.l;
     }
     __syncthreads();
-    if (kh == 1) return;
+    // the normalised rows of the plain path go out through LDS, stored by
+    // both key halves (below); other paths leave the writing to key half 0
+    if (kh == 1 && (TAPS || p.n_split > 1)) return;
+  }
+  if (KSPLIT == 2 && kh == 0) {
+    const float4 *xo = reinterpret_cast<const float4 *>(XATTN_KT(rg));
+    const float *xs = reinterpret_cast<const float *>(XATTN_VT(rg));
     const float m2 = xs[lane];
     const float l2 = xs[64 + lane];
     float a1 = 1.f, a2 = 0.f;
@@ -1146,8 +1152,6 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
         st.O[db][4 * j + 3] = st.O[db][4 * j + 3] * a1 + o2.w * a2;
       }
   }
-#undef XATTN_KT
-#undef XATTN_VT
 
   // ---- Merge / epilogue
   const int64_t n_rows_all = (int64_t)p.R * BW * p.Hq;
@@ -1213,12 +1217,57 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     for (int db = 0; db < NDB; ++db)
       st.O[db] = (st.O[db] * (inv_s * ws) + su.O[db] * (inv_u * wu)) * inv_z;
   } else {
-    const float lt = pair_sum(st.l);
-    const float inv = 1.f / lt;
-    if (valid && p.lse && hl == 0) p.lse[ri] = st.m * p.scale + __logf(lt);
+    if constexpr (KSPLIT == 2) {
+      // Row group rg's 32 normalised rows as bf16 in LDS (V tile of stage
+      // rg, past the exchanged m and l; row-major, 16-byte slots permuted by
+      // swz), then stored by both waves of the group as whole rows, 16
+      // bytes per lane: 64 / SLOTS rows per store instruction, where the
+      // accumulator layout would give 8 bytes of each of 32 rows.
+      static_assert(4096 + 32 * Gm::RB <= Gm::TILE_BYTES, "the staged rows must fit a V tile");
+      uint8_t *ost = tiles + (NSTAGE + rg) * Gm::TILE_BYTES + 4096;
+      if (kh == 0) {
+        const float lt = pair_sum(st.l);
+        const float inv = 1.f / lt;
+        if (valid && p.lse && hl == 0) p.lse[ri] = st.m * p.scale + __logf(lt);
+        const int osw = Gm::swz(ql);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) st.O[db] *= inv;
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x4 pk = {(__bf16)(st.O[db][4 * j + 0] * inv),
+                               (__bf16)(st.O[db][4 * j + 1] * inv),
+                               (__bf16)(st.O[db][4 * j + 2] * inv),
+                               (__bf16)(st.O[db][4 * j + 3] * inv)};
+            *reinterpret_cast<bf16x4 *>(ost + ql * Gm::RB + (((4 * db + j) ^ osw) << 4) +
+                                        hl * 8) = pk;
+          }
+      }
+      __syncthreads();
+      constexpr int NCH = 32 * Gm::SLOTS / (KSPLIT * 64);   // store instructions per wave
+#pragma unroll
+      for (int n = 0; n < NCH; ++n) {
+        const int idx = (n * KSPLIT + kh) * 64 + lane;
+        const int orow = idx / Gm::SLOTS, ch = idx % Gm::SLOTS;
+        const uint4 v =
+            *reinterpret_cast<const uint4 *>(ost + orow * Gm::RB + ((ch ^ Gm::swz(orow)) << 4));
+        const int grr = row0 + rg * 32 + orow;
+        if (grr < p.M) {
+          const int gb = grr / G;
+          const int64_t go = (((int64_t)r * BW + gb) * p.Hq + k * G + (grr - gb * G)) * D;
+          *reinterpret_cast<uint4 *>(og + go + ch * 8) = v;
+        }
+      }
+      return;
+    } else {
+      const float lt = pair_sum(st.l);
+      const float inv = 1.f / lt;
+      if (valid && p.lse && hl == 0) p.lse[ri] = st.m * p.scale + __logf(lt);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) st.O[db] *= inv;
+    }
   }
+#undef XATTN_KT
+#undef XATTN_VT
   if (!valid) return;
   uint16_t *op = og + qoff;
 #pragma unroll
