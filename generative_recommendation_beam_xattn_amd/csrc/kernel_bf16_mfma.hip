@@ -814,12 +814,21 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   const int beam = rr / G;
   const int64_t qoff = (((int64_t)r * BW + beam) * p.Hq + k * G + rr % G) * D;
   // stage 3 holds the q rows of row groups 0, 1 (K buffer) and 2, 3 (V
-  // buffer): NKS 1 KiB fragments per group, lane i's 16 bytes at 16 i
+  // buffer): the group's 32 rows laid out like a tile's (row-major, 16-byte
+  // slots permuted by swz), so that each copy reads ROWS_PER_COPY whole rows
+  // and the fragment reads below are free of bank conflicts
+  static_assert(32 * Gm::RB == NKS * 1024, "a row group's q rows are NKS 1 KiB copies");
   const uint8_t *qlds = tiles + ((rg < 2 ? 3 : NSTAGE + 3) * Gm::TILE_BYTES) +
-                        (rg & 1) * (NKS * 1024);
+                        (rg & 1) * (32 * Gm::RB);
   if (kh == 0) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) dma16(qg + qoff + ks * 16 + hl * 8, qlds + ks * 1024);
+    for (int n = 0; n < NKS; ++n) {
+      const int qr = n * Gm::ROWS_PER_COPY + lane / Gm::SLOTS;   // row of the group
+      const int qrr = min(row0 + rg * 32 + qr, p.M - 1);
+      const int qb = qrr / G;
+      const int64_t qro = (((int64_t)r * BW + qb) * p.Hq + k * G + (qrr - qb * G)) * D;
+      dma16(qg + qro + (((lane % Gm::SLOTS) ^ Gm::swz(qr)) << 3), qlds + n * 1024);
+    }
   }
 
   const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
@@ -919,7 +928,8 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   bf16x8 qf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8 *>(qlds + ks * 1024 + lane * 16);
+    qf[ks] = *reinterpret_cast<const bf16x8 *>(qlds + ql * Gm::RB +
+                                                (((2 * ks + hl) ^ Gm::swz(ql)) << 4));
   // rows of the two chunks the loop may copy (the last two steps), read
   // from LDS now, while no copy into LDS is in flight
   constexpr int B0PW = block0_copies_per_wave<D, WAVES>();
