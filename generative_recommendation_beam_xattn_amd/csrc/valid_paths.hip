@@ -32,6 +32,7 @@ namespace xattn {
 namespace {
 
 constexpr int kMaskThreads = 256;
+constexpr int kMaskBatch = 8;   // groups of 4 tokens a thread has in flight
 constexpr int kAdvanceThreads = 256;
 
 __device__ inline const int32_t *i32_at(const uint8_t *base, int64_t off) {
@@ -74,24 +75,39 @@ __global__ __launch_bounds__(kMaskThreads) void valid_mask_kernel(MaskParams p) 
     mrow = bits;
   }
 
-  // four tokens per step: a group that is all valid is left alone, an all
-  // invalid one is overwritten, a mixed one is blended
+  // four tokens per group: a group that is all valid is left alone, an all
+  // invalid one is overwritten, a mixed one is blended.  A thread takes
+  // kMaskBatch groups at a time and issues all their loads before the first
+  // store, so their latencies overlap.  The loads are unconditional (a
+  // branch around each would make the compiler wait for each one before
+  // the next): a group that needs no read loads the row's first 16 bytes
+  // instead, which every thread of the row shares in cache.
   const int n4 = V >> 2;
   const float ninf = -INFINITY;
-  for (int g = tid; g < n4; g += kMaskThreads) {
-    const int j = g << 2;
-    const uint32_t nib = (mrow[j >> 5] >> (j & 31)) & 0xFu;
-    if (nib == 0xFu) continue;
-    float4 *dst = reinterpret_cast<float4 *>(lg + j);
-    if (nib == 0u) {
-      *dst = make_float4(ninf, ninf, ninf, ninf);
-    } else {
-      float4 v = *dst;
-      if (!(nib & 1u)) v.x = ninf;
-      if (!(nib & 2u)) v.y = ninf;
-      if (!(nib & 4u)) v.z = ninf;
-      if (!(nib & 8u)) v.w = ninf;
-      *dst = v;
+  for (int g0 = tid; g0 < n4; g0 += kMaskThreads * kMaskBatch) {
+    uint32_t nib[kMaskBatch];
+    float4 v[kMaskBatch];
+#pragma unroll
+    for (int u = 0; u < kMaskBatch; ++u) {
+      const int g = g0 + u * kMaskThreads;
+      const int j = g << 2;
+      nib[u] = g < n4 ? (mrow[j >> 5] >> (j & 31)) & 0xFu : 0xFu;
+      const bool mixed = nib[u] != 0xFu && nib[u] != 0u;
+      v[u] = *reinterpret_cast<const float4 *>(lg + (mixed ? j : 0));
+    }
+#pragma unroll
+    for (int u = 0; u < kMaskBatch; ++u) {
+      const int j = (g0 + u * kMaskThreads) << 2;
+      if (nib[u] == 0xFu) continue;
+      float4 w = make_float4(ninf, ninf, ninf, ninf);
+      if (nib[u] != 0u) {
+        w = v[u];
+        if (!(nib[u] & 1u)) w.x = ninf;
+        if (!(nib[u] & 2u)) w.y = ninf;
+        if (!(nib[u] & 4u)) w.z = ninf;
+        if (!(nib[u] & 8u)) w.w = ninf;
+      }
+      *reinterpret_cast<float4 *>(lg + j) = w;
     }
   }
   for (int j = (n4 << 2) + tid; j < V; j += kMaskThreads)
