@@ -15,7 +15,8 @@
 // workgroup touches those bytes.  Splitting the slice by K/V and columns
 // spreads a level's few slices over many workgroups.  Rows whose parent is
 // themselves are not rewritten, and a slice whose parents are all the
-// identity is left untouched without a read.
+// identity is not written at all (its rows are read with the parents, in
+// the same round trip).
 #include <hip/hip_ext.h>
 
 #include "xattn_internal.h"
@@ -25,7 +26,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStageBytes = 32 * 1024;
+static_assert(kStageBytes <= kThreads * 8 * 16, "8 units per thread cover the stage");
+static_assert(kMaxReorderBeams <= kThreads * 8, "8 parent slots per thread cover the beams");
 
+// UPT: 16-byte units of the stage per thread, PPT: parent slots per thread
+// (each the smallest power of two that covers the launch), so every thread
+// issues all of its loads before it waits and none of them is redundant.
+template <int UPT, int PPT>
 __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytes];
   __shared__ int moved;
@@ -41,32 +48,55 @@ __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParam
   const int r = rk / p.Hkv;
   const int BW = p.BW;
 
-  if (tid == 0) moved = 0;
-  __syncthreads();
-  int mine = 0;
-  for (int b = tid; b < BW; b += kThreads) {
-    const int a = min(max(p.parent[(int64_t)r * p.parent_stride + b], 0), BW - 1);
-    par[b] = a;
-    mine |= a != b;
-  }
-  if (mine) moved = 1;   // benign race: every writer stores 1
-  __syncthreads();
-  if (!moved) return;
-
   const int64_t RB = p.row_bytes;                        // bytes of one row
   const int64_t slice = (((int64_t)r * p.Hkv + k) * p.S + t) * BW * RB;
   const int units_per_row = (int)(p.chunk_bytes / 16);    // 16-byte units per row per chunk
   const int n_units = BW * units_per_row;
   uint8_t *base = static_cast<uint8_t *>(part < n_cc ? p.unshared_k : p.unshared_v) + slice;
   const int64_t c0 = (int64_t)(part % n_cc) * p.chunk_bytes;
-  // stage columns [c0, c0 + chunk) of every row of the slice
-  for (int u = tid; u < n_units; u += kThreads) {
-    const int b = u / units_per_row, c = u - b * units_per_row;
-    *reinterpret_cast<uint4 *>(stage + (int64_t)u * 16) =
-        *reinterpret_cast<const uint4 *>(base + (int64_t)b * RB + c0 + c * 16);
+
+  // The parent slots and columns [c0, c0 + chunk) of every row of the slice
+  // are loaded together (one memory round trip, not one for the parents and
+  // then one for the rows).
+  if (tid == 0) moved = 0;
+  // this thread's parent slots, loaded into registers first and stored to
+  // LDS only after the row loads are issued (indices past BW repeat the
+  // last slot and are not stored)
+  int32_t pr[PPT];
+#pragma unroll
+  for (int i = 0; i < PPT; ++i)
+    pr[i] = p.parent[(int64_t)r * p.parent_stride + min(tid + i * kThreads, BW - 1)];
+  {
+    uint4 v[UPT];
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = min(tid + i * kThreads, n_units - 1);
+      const int b = u / units_per_row, c = u - b * units_per_row;
+      v[i] = *reinterpret_cast<const uint4 *>(base + (int64_t)b * RB + c0 + c * 16);
+    }
+    // (units past the end, in the last round only, repeat the last one: the
+    // same bytes to the same place, with no branch to hold the loads apart)
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = min(tid + i * kThreads, n_units - 1);
+      *reinterpret_cast<uint4 *>(stage + (int64_t)u * 16) = v[i];
+    }
   }
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < PPT; ++i) {
+    const int b = tid + i * kThreads;
+    if (b < BW) {
+      const int a = min(max(pr[i], 0), BW - 1);
+      par[b] = a;
+      mine |= a != b;
+    }
+  }
+  __syncthreads();   // moved = 0 is visible before any thread sets it
+  if (mine) moved = 1;   // benign race: every writer stores 1
   __syncthreads();
-  // every read of this chunk is done: write the moved rows
+  if (!moved) return;
+  // every read of this chunk is done (the barriers above): write the moved rows
   for (int u = tid; u < n_units; u += kThreads) {
     const int b = u / units_per_row, c = u - b * units_per_row;
     const int a = par[b];
@@ -87,12 +117,32 @@ hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, L
       (int64_t)p.BW * p.chunk_bytes > kStageBytes || p.chunk_bytes % 16 != 0 ||
       p.row_bytes % p.chunk_bytes != 0)
     return hipErrorInvalidConfiguration;
-  if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(reorder_unshared_kernel, dim3((unsigned)grid), dim3(kThreads),
-                          (size_t)p.BW * sizeof(int32_t), stream, ev.start, ev.stop, 0u, p);
-  else
-    hipLaunchKernelGGL(reorder_unshared_kernel, dim3((unsigned)grid), dim3(kThreads),
-                       (size_t)p.BW * sizeof(int32_t), stream, p);
+  auto pow2_cover = [](int64_t n) {   // smallest of 1, 2, 4, 8 with 256 * it >= n
+    int x = 1;
+    while (x < 8 && (int64_t)x * kThreads < n) x *= 2;
+    return x;
+  };
+  const int upt = pow2_cover((int64_t)p.BW * (p.chunk_bytes / 16));
+  const int ppt = pow2_cover(p.BW) == 1 ? 1 : 8;
+  auto go = [&](auto kernel) {
+    if (ev.start || ev.stop)
+      hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads),
+                            (size_t)p.BW * sizeof(int32_t), stream, ev.start, ev.stop, 0u, p);
+    else
+      hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads),
+                         (size_t)p.BW * sizeof(int32_t), stream, p);
+  };
+  if (ppt == 1) {
+    if (upt == 1) go(reorder_unshared_kernel<1, 1>);
+    else if (upt == 2) go(reorder_unshared_kernel<2, 1>);
+    else if (upt == 4) go(reorder_unshared_kernel<4, 1>);
+    else go(reorder_unshared_kernel<8, 1>);
+  } else {
+    if (upt == 1) go(reorder_unshared_kernel<1, 8>);
+    else if (upt == 2) go(reorder_unshared_kernel<2, 8>);
+    else if (upt == 4) go(reorder_unshared_kernel<4, 8>);
+    else go(reorder_unshared_kernel<8, 8>);
+  }
   return hipGetLastError();
 }
 
