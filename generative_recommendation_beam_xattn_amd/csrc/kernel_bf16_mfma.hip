@@ -362,6 +362,24 @@ __device__ __forceinline__ float softmax_max(f32x16 (&sacc)[2 / KSPLIT], Rows<D>
   return st.m == -INFINITY ? 0.f : st.m * c;
 }
 
+// Part 1 for a tile whose row maxima were already taken (tmax: this lane's
+// maximum over its scores of the tile, no masking): combine the lane pair
+// and raise m lazily.  Returns m * c, as softmax_max.
+template <int D>
+__device__ __forceinline__ float softmax_max_finish(float tmax, Rows<D> &st, float c, float thr) {
+  constexpr int NDB = D / 32;
+  tmax = pair_max(tmax);
+  if (__any(tmax > st.m + thr)) {
+    const float mn = fmaxf(st.m, tmax);
+    const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((st.m - mn) * c);
+    st.m = mn;
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) st.O[db] *= alpha;
+  }
+  return st.m == -INFINITY ? 0.f : st.m * c;
+}
+
 // Part 2 (branch-free): probabilities exp2(s * c - mc) as bf16 (the B
 // operand of the PV product) and their sum into l, two per
 // v_dot2_f32_bf16 against (1, 1), so l sums exactly the values PV uses.
@@ -471,6 +489,52 @@ __device__ __forceinline__ void pv_tile(const uint8_t *vt, const bf16x8 (&pf)[4 
   for (int n = 0; n < NSTEP; ++n) {
     if (n + kFragAhead < NSTEP) a[n + kFragAhead] = frag(n + kFragAhead);
     st.O[n % NDB] = mfma(a[n], pf[n / NDB], st.O[n % NDB]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// pv_tile with the next tile's row maxima taken between its MFMAs: this
+// lane's maximum over s_next (no masking) into tmax, one max3 per k-step
+// from the second on, so the VALU works while the matrix core runs and the
+// next step starts with only the lane-pair exchange left.
+template <int D, int KSPLIT>
+__device__ __forceinline__ void pv_tile_max(const uint8_t *vt, const bf16x8 (&pf)[4 / KSPLIT],
+                                            Rows<D> &st, int kh, const FragOffsets<D> &fo,
+                                            const f32x16 (&s_next)[2 / KSPLIT], float &tmax) {
+  using Gm = TileGeom<D>;
+  constexpr int NDB = D / 32, NKB = 2 / KSPLIT;
+  const uint8_t *vbase = vt + kh * NKB * 32 * Gm::RB;
+  constexpr int NSTEP = 2 * NKB * NDB;
+  constexpr int NV = 16 * NKB;                      // scores per lane
+  constexpr int PER = (NV + NSTEP - 2) / (NSTEP - 1);   // scores per k-step, steps 1..NSTEP-1
+  static_assert(NSTEP >= 2, "maxima start at the second k-step");
+  auto frag = [&](int n) {
+    const int j2 = n / NDB, db = n % NDB;
+    const int prow = (j2 >> 1) * 32 + (j2 & 1) * 16;
+    const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(vbase + fo.v[0][db] + prow * Gm::RB));
+    const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(vbase + fo.v[1][db] + prow * Gm::RB));
+    return bf16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  };
+  bf16x8 a[NSTEP];
+#pragma unroll
+  for (int j = 0; j < kFragAhead && j < NSTEP; ++j) a[j] = frag(j);
+  tmax = -INFINITY;
+#pragma unroll
+  for (int n = 0; n < NSTEP; ++n) {
+    if (n + kFragAhead < NSTEP) a[n + kFragAhead] = frag(n + kFragAhead);
+    st.O[n % NDB] = mfma(a[n], pf[n / NDB], st.O[n % NDB]);
+    if (n >= 1 && (n - 1) * PER < NV) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int v = (n - 1) * PER + u;
+        if (v < NV) tmax = fmaxf(tmax, s_next[v >> 4][v & 15]);
+      }
+      // pins this share of the maxima here: IR passes would otherwise sink
+      // the pure max chain past the scheduling fence to its use
+      asm volatile("" : "+v"(tmax));
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -999,6 +1063,13 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   f32x16 s_cur[NKB], s_next[NKB];
   bf16x8 pf[2 * NKB];
   if (n_tiles > 0) qk_tile<D, KSPLIT>(XATTN_KT(0), qf, s_cur, fo);
+  // this lane's maximum over the scores of the tile the next loop step
+  // consumes (loop tiles are never masked: only the last tile is)
+  float tmax_cur = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NKB; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tmax_cur = fmaxf(tmax_cur, s_cur[i][e]);
 // whether step u's end copied something (tile u + 3, or chunk u - chunk_t0;
 // at most two chunks are copied in the loop)
 #define XATTN_COPIED(u) \
@@ -1024,10 +1095,10 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       }                                                                               \
     }                                                                                 \
     lds_barrier();                                                                    \
-    const float mc = softmax_max<D, KSPLIT, false>(s_cur, st, kh, 0, 0, L, c, thr, lane); \
+    const float mc = softmax_max_finish<D>(tmax_cur, st, c, thr);                     \
     qk_next_with_exp<D, KSPLIT>(XATTN_KT(((ST) + 1) % NSTAGE), qf, s_next, s_cur, pf, st, \
                                 c, mc, fo);                                           \
-    pv_tile<D, KSPLIT>(XATTN_VT(ST), pf, st, kh, fo);                                 \
+    pv_tile_max<D, KSPLIT>(XATTN_VT(ST), pf, st, kh, fo, s_next, tmax_cur);           \
     if (t + 3 < n_tiles)                                                              \
       tile_copy<D, WAVES, false>(XATTN_KT(((ST) + 3) % NSTAGE),                       \
                                  XATTN_VT(((ST) + 3) % NSTAGE), cplan, skg, svg,      \
