@@ -967,48 +967,76 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
 #define XATTN_SK (tiles + 2 * NSTAGE * Gm::TILE_BYTES)
 #define XATTN_SV (tiles + 2 * NSTAGE * Gm::TILE_BYTES + 32 * Gm::RB)
 
-  // ---- wait for tile 0 (the parent rows and q are older, so they are in
-  // too), then the ancestor slots of the block's beams (short chains:
-  // walked here, from the parent rows staged in LDS)
-  if (n_tiles > 2)
-    wait_vm_lgkm0<2 * CPW>();
-  else if (n_tiles > 1)
-    wait_vm_lgkm0<CPW>();
-  else
-    wait_vm_lgkm0<0>();
-  if (staged) lds_barrier();   // every wave's parent copies have landed
-  if (walk_here) {
-    for (int i = tid; i < nb; i += NT) {
-      int a = b_lo + i;
-      int32_t *dst = anc_lds + i * (step + 1);
-      dst[step] = a;
-      for (int t = step; t >= 1; --t) {
-        a = clampi(staged ? par_lds[(t - 1) * BW + a] : par[(int64_t)t * BW + a], 0, BW - 1);
-        dst[t - 1] = a;
-      }
-    }
+  constexpr int B0PW = block0_copies_per_wave<D, WAVES>();
+  // rows of the two chunks the loop may copy (the last two steps), read
+  // from LDS once the ancestor slots are in (two named arrays: an array
+  // indexed by a runtime chunk number would live in scratch memory)
+  int chunk_rows0[CopyPlan<D, WAVES>::PER], chunk_rows1[CopyPlan<D, WAVES>::PER];
+// (macros, not lambdas: a lambda capturing the LDS ring turns its address
+// into a generic pointer, and the cast back in the copies miscompiles)
+#define XATTN_WALK()                                                                  \
+  for (int i = tid; i < nb; i += NT) {                                                \
+    int a = b_lo + i;                                                                 \
+    int32_t *dst = anc_lds + i * (step + 1);                                          \
+    dst[step] = a;                                                                    \
+    for (int t = step; t >= 1; --t) {                                                 \
+      a = clampi(staged ? par_lds[(t - 1) * BW + a] : par[(int64_t)t * BW + a], 0, BW - 1); \
+      dst[t - 1] = a;                                                                 \
+    }                                                                                 \
   }
-  lds_barrier();  // tile 0, q and the ancestor slots are visible
+#define XATTN_ISSUE_BLOCK0()                                                          \
+  {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < CopyPlan<D, WAVES>::PER; ++i) {             \
+      const int row = CopyPlan<D, WAVES>::row_of(cplan.off[i]);                       \
+      chunk_rows0[i] = tmap.row_index(1 + row / 32, row % 32);                        \
+      chunk_rows1[i] = tmap.row_index(3 + row / 32, row % 32);                        \
+    }                                                                                 \
+    token_block0_copy<D, WAVES>(XATTN_SK, XATTN_SV, ukg, uvg, tmap, wave, lane);      \
+  }
+  // On the common path (the first three tiles copied speculatively, parent
+  // rows staged) the walk waits for the parent rows alone, the oldest
+  // copies: it and the copy of token block 0 then run under the latency of
+  // tile 0 instead of after it.  The wait leaves this wave's q copies
+  // (key half 0) and its three tiles' copies in flight, which the vmcnt
+  // field must be able to count.
+  constexpr bool kEarlyWalkFits = 3 * CPW + NKS < 64;
+  const bool early_walk = kEarlyWalkFits && staged && lds_tokens && speculate && n_tiles > 3;
+  if (early_walk) {
+    if constexpr (kEarlyWalkFits) {
+      if (kh == 0)
+        wait_vm_lgkm0<3 * CPW + NKS>();
+      else
+        wait_vm_lgkm0<3 * CPW>();
+    }
+    lds_barrier();   // every wave's parent copies have landed
+    XATTN_WALK()
+    lds_barrier();   // the ancestor slots are visible
+    XATTN_ISSUE_BLOCK0()
+    // tile 0 and q, older than tiles 1, 2 and block 0
+    wait_vm_lgkm0<2 * CPW + B0PW>();
+    lds_barrier();   // tile 0 and q are visible
+  } else {
+    // ---- wait for tile 0 (the parent rows and q are older, so they are in
+    // too), then the ancestor slots of the block's beams (short chains:
+    // walked here, from the parent rows staged in LDS)
+    if (n_tiles > 2)
+      wait_vm_lgkm0<2 * CPW>();
+    else if (n_tiles > 1)
+      wait_vm_lgkm0<CPW>();
+    else
+      wait_vm_lgkm0<0>();
+    if (staged) lds_barrier();   // every wave's parent copies have landed
+    if (walk_here) XATTN_WALK()
+    lds_barrier();  // tile 0, q and the ancestor slots are visible
+    if (lds_tokens) XATTN_ISSUE_BLOCK0()
+  }
+#undef XATTN_WALK
+#undef XATTN_ISSUE_BLOCK0
   bf16x8 qf[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8 *>(qlds + ql * Gm::RB +
                                                 (((2 * ks + hl) ^ Gm::swz(ql)) << 4));
-  // rows of the two chunks the loop may copy (the last two steps), read
-  // from LDS now, while no copy into LDS is in flight
-  constexpr int B0PW = block0_copies_per_wave<D, WAVES>();
-  // (two named arrays: an array indexed by a runtime chunk number would
-  // live in scratch memory)
-  int chunk_rows0[CopyPlan<D, WAVES>::PER], chunk_rows1[CopyPlan<D, WAVES>::PER];
-  if (lds_tokens) {
-#pragma unroll
-    for (int i = 0; i < CopyPlan<D, WAVES>::PER; ++i) {
-      const int row = CopyPlan<D, WAVES>::row_of(cplan.off[i]);
-      chunk_rows0[i] = tmap.row_index(1 + row / 32, row % 32);
-      chunk_rows1[i] = tmap.row_index(3 + row / 32, row % 32);
-    }
-    token_block0_copy<D, WAVES>(XATTN_SK, XATTN_SV, ukg, uvg, tmap, wave, lane);
-  }
 
   Rows<D> st;
   st.clear();
