@@ -57,6 +57,10 @@ SMALL = {
     "deep_segmented_walk": dict(R=2, BW=40, Hq=4, Hkv=2, D=128, L=[100, 20], steps=[150],
                                 S=151),
     "deep_segmented_wide": dict(R=1, BW=300, Hq=2, Hkv=2, D=64, L=[40], steps=[100], S=101),
+    # the ancestor walk under tile 0's latency (prompts of more than three
+    # tiles, parent rows staged): 64-row workgroups, and head_dim 64
+    "early_walk_rg2": dict(R=2, BW=12, Hq=8, Hkv=2, D=128, L=[700, 257], steps=[1, 2], S=3),
+    "early_walk_d64": dict(R=2, BW=24, Hq=8, Hkv=2, D=64, L=[450, 300], steps=[2], S=3),
     "single_beam_empty_prompt": dict(R=2, BW=1, Hq=4, Hkv=1, D=128, L=[0, 0], steps=[0]),
     "no_shared_rows": dict(R=2, BW=3, Hq=4, Hkv=2, D=64, L=[0, 0], steps=[1], Lmax=0),
     # either side of the row count below which bf16 calls go to the per-beam
