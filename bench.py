@@ -15,8 +15,11 @@ Prints ONE JSON line.  `value` is beam-steps per second over the timed
 region (wall clock between two device synchronisations).  `roofline` covers
 the decode kernel: algorithmic bytes (unique KV rows + q + out + indices) or
 FLOPs per launch divided by the kernel's mean launch duration, measured with
-a pair of HIP events bound to each kernel dispatch (xattn_decode_timed), so
-the duration is the kernel's own, as a kernel trace reports it.
+a pair of HIP events bound to the kernel dispatch (xattn_decode_timed), so
+the duration is the kernel's own, as a kernel trace reports it.  The events
+are bound to the calls of every n-th step of the timed region (--time-every,
+default 4): their markers cost the GPU about 4 us per launch, which binding
+them to every call would charge to the throughput.
 `cpu_baseline` times the float64 CPU oracle on the host cores on a bounded
 sample of the same workload.  After the timed region, two side legs time
 other kernels on the same device: `per_beam_comparison` (the per-beam
@@ -57,6 +60,10 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--G", type=int, default=None, help="prefix group size for config 5")
     ap.add_argument("--rot", type=int, default=None, help="rotation copies (default: >= 1 GB)")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="bind timing events to the calls of every n-th timed step (the events "
+                         "cost the GPU about 4 us per launch, so binding them to every call would "
+                         "charge them to the throughput)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -365,15 +372,17 @@ def main():
 
     for k in range(args.warmup):
         run_step(k)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
-          for _ in range(args.steps)]
-    for row in ev:          # torch creates the HIP event at its first record
+    every = max(1, args.time_every)
+    timed_steps = [k for k in range(args.steps) if k % every == 0]
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
+          for k in timed_steps}
+    for row in ev.values():   # torch creates the HIP event at its first record
         for e in row:
             e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        run_step(args.warmup + k, ev[k])
+        run_step(args.warmup + k, ev.get(k))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
@@ -388,7 +397,7 @@ def main():
 
     # per-launch durations (ms) of each decode call, by level
     per_call = np.array([[ev[k][2 * i].elapsed_time(ev[k][2 * i + 1]) for i in range(n_calls)]
-                         for k in range(args.steps)])
+                         for k in timed_steps])
     mean_launch_s = per_call.mean(axis=0) / 1e3
 
     # the per-beam (PagedAttention-style) comparison kernel on the same inputs,
@@ -460,7 +469,9 @@ def main():
                                  "by_level": [float(x * 1e6) for x in mean_launch_s],
                                  "p10": float(np.percentile(per_call, 10) * 1e3),
                                  "p50": float(np.percentile(per_call, 50) * 1e3),
-                                 "p90": float(np.percentile(per_call, 90) * 1e3)},
+                                 "p90": float(np.percentile(per_call, 90) * 1e3),
+                                 "launches_timed": int(per_call.size),
+                                 "every_nth_step": every},
         "algorithmic_per_launch": {"bytes": bytes_per_launch, "unique_kv_bytes": ukv_per_launch,
                                    "flops": flops_per_launch},
         "kernel_sha256_16": kernel_digest(w.dtype),
