@@ -153,8 +153,11 @@ xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const v
  * kernel's, stop to the last one's -- so hipEventElapsedTime(start_event,
  * stop_event) is the call's execution time on the device, with no queue or
  * marker latency around it.  A call is one kernel, or for chains deeper than
- * 16 levels up to three (ancestor slots, the Unshared stage for bf16, then
- * attention).
+ * 16 levels up to five (the ancestor slots in one or two kernels, the
+ * Unshared stage for bf16, attention, and the merge of key splits when the
+ * grid is small).  Binding the events costs the device a few microseconds per
+ * call around the dispatch, so a caller measuring throughput times a sample
+ * of its calls this way and issues the rest through xattn_decode.
  * Returns XATTN_EINVAL if an event is NULL.
  */
 xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const void *shared_k,
