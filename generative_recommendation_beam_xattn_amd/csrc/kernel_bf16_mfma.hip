@@ -204,6 +204,11 @@ struct TileGeom {
   }
 };
 
+// Distance from a ring stage's K tile to its V tile (the V tiles of all
+// stages follow the K tiles of all stages).
+template <int D>
+__host__ __device__ constexpr int kVRegionOffset() { return NSTAGE * TileGeom<D>::TILE_BYTES; }
+
 // This wave's share of the COPIES wave-wide copies that fill one stage:
 // copy i moves 1 KiB = ROWS_PER_COPY rows of the K tile (first NQ copies)
 // or of the V tile.  Lane `lane` fetches row q * ROWS_PER_COPY + lane /
@@ -292,6 +297,11 @@ struct FragOffsets {
     for (int ks = 0; ks < D / 16; ++ks)
       k[ks] = (uint32_t)((kh * nkb * 32 + ql) * Gm::RB + (((2 * ks + hl) ^ kswz) << 4));
     const int vh = lane >> 5, vg = (lane >> 4) & 1, vj = lane & 15;
+    // the V offsets carry the key half's rows and the distance from the K
+    // tiles to the V tiles of the ring, so that a V fragment's address is
+    // (ring stage base + this register + an immediate below 64 KiB): the
+    // V tiles themselves lie past the 16-bit offset field
+    const int kv_region = kVRegionOffset<D>();
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       const int row = e2 * 8 + vh * 4 + (vj >> 2);   // plus multiples of 16
@@ -299,7 +309,8 @@ struct FragOffsets {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int chunk = 4 * db + 2 * vg + ((vj >> 1) & 1);
-        v[e2][db] = (uint32_t)(row * Gm::RB + ((chunk ^ sw) << 4) + ((vj & 1) << 3));
+        v[e2][db] = (uint32_t)(kv_region + (kh * nkb * 32 + row) * Gm::RB + ((chunk ^ sw) << 4) +
+                               ((vj & 1) << 3));
       }
     }
   }
@@ -470,7 +481,7 @@ __device__ __forceinline__ void pv_tile(const uint8_t *vt, const bf16x8 (&pf)[4 
                                         Rows<D> &st, int kh, const FragOffsets<D> &fo) {
   using Gm = TileGeom<D>;
   constexpr int NDB = D / 32, NKB = 2 / KSPLIT;
-  const uint8_t *vbase = vt + kh * NKB * 32 * Gm::RB;
+  const uint8_t *vbase = vt - kVRegionOffset<D>();   // fo.v holds the rest (and kh's rows)
   constexpr int NSTEP = 2 * NKB * NDB;
   // fragment n: k-step j2 = n / NDB (rows 32*(j2/2) + 16*(j2%2)), block db = n % NDB
   auto frag = [&](int n) {
@@ -503,7 +514,7 @@ __device__ __forceinline__ void pv_tile_max(const uint8_t *vt, const bf16x8 (&pf
                                             const f32x16 (&s_next)[2 / KSPLIT], float &tmax) {
   using Gm = TileGeom<D>;
   constexpr int NDB = D / 32, NKB = 2 / KSPLIT;
-  const uint8_t *vbase = vt + kh * NKB * 32 * Gm::RB;
+  const uint8_t *vbase = vt - kVRegionOffset<D>();   // fo.v holds the rest (and kh's rows)
   constexpr int NSTEP = 2 * NKB * NDB;
   constexpr int NV = 16 * NKB;                      // scores per lane
   constexpr int PER = (NV + NSTEP - 2) / (NSTEP - 1);   // scores per k-step, steps 1..NSTEP-1
