@@ -517,7 +517,8 @@ __device__ __forceinline__ void pv_tile_max(const uint8_t *vt, const bf16x8 (&pf
   const uint8_t *vbase = vt - kVRegionOffset<D>();   // fo.v holds the rest (and kh's rows)
   constexpr int NSTEP = 2 * NKB * NDB;
   constexpr int NV = 16 * NKB;                      // scores per lane
-  constexpr int PER = (NV + NSTEP - 2) / (NSTEP - 1);   // scores per k-step, steps 1..NSTEP-1
+  // scores per k-step (steps 1..NSTEP-1), even: two per v_max3_f32
+  constexpr int PER = ((NV + NSTEP - 2) / (NSTEP - 1) + 1) & ~1;
   static_assert(NSTEP >= 2, "maxima start at the second k-step");
   auto frag = [&](int n) {
     const int j2 = n / NDB, db = n % NDB;
@@ -537,14 +538,21 @@ __device__ __forceinline__ void pv_tile_max(const uint8_t *vt, const bf16x8 (&pf
     if (n + kFragAhead < NSTEP) a[n + kFragAhead] = frag(n + kFragAhead);
     st.O[n % NDB] = mfma(a[n], pf[n / NDB], st.O[n % NDB]);
     if (n >= 1 && (n - 1) * PER < NV) {
+      // two scores per v_max3_f32, issued here: as plain fmaxf the IR passes
+      // sink the pure max chain past the scheduling fence to its use, and a
+      // chain broken at each step costs a quieting max per operand (scores
+      // are finite or -inf, never NaN, so the ordering of v_max3 is exact)
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
+      for (int u = 0; u < PER; u += 2) {
         const int v = (n - 1) * PER + u;
-        if (v < NV) tmax = fmaxf(tmax, s_next[v >> 4][v & 15]);
+        if (v + 1 < NV) {
+          asm volatile("v_max3_f32 %0, %0, %1, %2"
+                       : "+v"(tmax)
+                       : "v"(s_next[v >> 4][v & 15]), "v"(s_next[(v + 1) >> 4][(v + 1) & 15]));
+        } else if (v < NV) {
+          asm volatile("v_max_f32 %0, %0, %1" : "+v"(tmax) : "v"(s_next[v >> 4][v & 15]));
+        }
       }
-      // pins this share of the maxima here: IR passes would otherwise sink
-      // the pure max chain past the scheduling fence to its use
-      asm volatile("" : "+v"(tmax));
     }
     __builtin_amdgcn_sched_barrier(0);
   }
