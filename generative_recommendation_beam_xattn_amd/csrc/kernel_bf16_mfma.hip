@@ -115,6 +115,14 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4));
 }
 
+// LDS byte address of a generic pointer into LDS: its low 32 bits (the LDS
+// aperture keeps the offset there).  Taken directly rather than through an
+// address-space cast, whose null check the compiler has miscompiled here
+// (an illegal compare against the shared aperture base).
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
 // One wave-wide 16-byte-per-lane copy global -> LDS (global_load_lds): lane
 // i's 16 bytes at src land at LDS byte address lds_base + 16 i.  Issued as
 // inline asm so that the compiler does not see the LDS write: it would
@@ -124,8 +132,7 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 // preceded by an explicit vmcnt wait and a barrier; the copy counts in vmcnt
 // like any load, in issue order.
 __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(lds_dst));
   uint32_t saved;  // M0 is the compiler's: put it back
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -141,8 +148,7 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
 // byte offset (the instruction's saddr form): no per-lane 64-bit address
 // arithmetic on the vector ALUs.
 __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, const void *lds_dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(lds_dst));
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -157,8 +163,7 @@ __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, const v
 // The same for 4 bytes per lane (global_load_lds_dword): lane i's 4 bytes
 // at src land at LDS byte address lds_base + 4 i.
 __device__ __forceinline__ void dma4(const void *src, const void *lds_dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)lds_dst);
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(lds_dst));
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -438,7 +443,6 @@ __device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf1
   constexpr int NV = 16 * NKB;        // scores per lane
   constexpr int PER = NV / NKS;       // exponentials per k-step (even)
   static_assert(PER % 2 == 0, "scores are packed in pairs");
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int i = 0; i < NKB; ++i) s_next[i] = f32x16{};
   bf16x8 a[NKS][NKB];   // indexed by unrolled constants only: registers
@@ -465,7 +469,12 @@ __device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf1
       const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
       pf[v >> 3][v & 7] = pk[0];
       pf[v >> 3][(v + 1) & 7] = pk[1];
-      st.l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, st.l, false);
+      // the row sum, issued here under the MFMA (as a plain intrinsic the
+      // IR passes sink the whole chain to the step's end, where nothing
+      // hides it): l += 1 * p0 + 1 * p1 on the packed pair
+      asm volatile("v_dot2c_f32_bf16 %0, 0x3f803f80, %1"
+                   : "+v"(st.l)
+                   : "v"(__builtin_bit_cast(uint32_t, pk)));
     }
     __builtin_amdgcn_sched_barrier(0);
   }
