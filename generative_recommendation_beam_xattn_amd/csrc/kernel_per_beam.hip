@@ -24,6 +24,7 @@ namespace xattn {
 namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerPass = 4;   // query rows a pass keeps state for
@@ -158,8 +159,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
           kr = ukg + e;
           vr = uvg + e;
         }
-        kvu[u] = *reinterpret_cast<const uint4 *>(kr + part * 8);
-        vvu[u] = *reinterpret_cast<const uint4 *>(vr + part * 8);
+        // each K/V row is read once per workgroup: streamed past the caches
+        kvu[u] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kr + part * 8)));
+        vvu[u] = __builtin_bit_cast(
+            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vr + part * 8)));
       }
       // scores of the keys in flight against the pass's query rows (a key
       // past the end scores -inf and adds nothing)
