@@ -137,7 +137,7 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(base)
@@ -153,7 +153,7 @@ __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, const v
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(sbase), "s"(base)
