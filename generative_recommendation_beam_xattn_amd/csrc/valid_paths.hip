@@ -31,6 +31,10 @@
 namespace xattn {
 namespace {
 
+// masked logits are written once, past the caches (non-temporal stores);
+// the loads stay cached: groups that need no read all load the row's start
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kMaskThreads = 256;
 constexpr int kMaskBatch = 8;   // groups of 4 tokens a thread has in flight
 constexpr int kAdvanceThreads = 256;
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kMaskThreads) void valid_mask_kernel(MaskParams p) 
         if (!(nib[u] & 4u)) w.z = ninf;
         if (!(nib[u] & 8u)) w.w = ninf;
       }
-      *reinterpret_cast<float4 *>(lg + j) = w;
+      __builtin_nontemporal_store(__builtin_bit_cast(f32x4, w), reinterpret_cast<f32x4 *>(lg + j));
     }
   }
   for (int j = (n4 << 2) + tid; j < V; j += kMaskThreads)
