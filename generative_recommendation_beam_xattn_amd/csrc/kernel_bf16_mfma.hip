@@ -57,6 +57,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int KT = 64;      // keys per shared-stage tile
@@ -1391,7 +1392,9 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
         if (grr < p.M) {
           const int gb = grr / G;
           const int64_t go = (((int64_t)r * BW + gb) * p.Hq + k * G + (grr - gb * G)) * D;
-          *reinterpret_cast<uint4 *>(og + go + ch * 8) = v;
+          // written once: past the caches (non-temporal)
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                      reinterpret_cast<u32x4 *>(og + go + ch * 8));
         }
       }
       return;
