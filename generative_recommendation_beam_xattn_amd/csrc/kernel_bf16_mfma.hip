@@ -1503,10 +1503,16 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p) {
   }
   const float inv = 1.f / l;
   uint16_t *op = static_cast<uint16_t *>(p.out) + ri * D + lane * PER;
+  if constexpr (PER == 2) {
+    // the lane's two values as one 4-byte store, written once (non-temporal)
+    const bf16x2 v = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv)};
+    __builtin_nontemporal_store(__builtin_bit_cast(uint32_t, v), reinterpret_cast<uint32_t *>(op));
+  } else {
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const __bf16 v = (__bf16)(acc[k] * inv);
-    op[k] = *reinterpret_cast<const uint16_t *>(&v);
+    for (int k = 0; k < PER; ++k) {
+      const __bf16 v = (__bf16)(acc[k] * inv);
+      op[k] = *reinterpret_cast<const uint16_t *>(&v);
+    }
   }
   if (p.lse && lane == 0) p.lse[ri] = m * p.scale + __logf(l);
 }
