@@ -132,33 +132,56 @@ __device__ __forceinline__ uint32_t lds_address(const void *p) {
 // information), draining the tile pipeline.  Every use of copied data is
 // preceded by an explicit vmcnt wait and a barrier; the copy counts in vmcnt
 // like any load, in issue order.
+// NT: with the non-temporal hint (data no other workgroup reads soon).
+template <bool NT = true>
 __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(lds_dst));
   uint32_t saved;  // M0 is the compiler's: put it back
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(base)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base)
+        : "memory");
 }
 
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
 // byte offset (the instruction's saddr form): no per-lane 64-bit address
 // arithmetic on the vector ALUs.
+template <bool NT = true>
 __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, const void *lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(lds_dst));
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(sbase), "s"(base)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(base)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(base)
+        : "memory");
 }
 
 // The same for 4 bytes per lane (global_load_lds_dword): lane i's 4 bytes
@@ -244,7 +267,7 @@ struct CopyPlan {
 // shifted back to end at L), so only a prompt shorter than one tile needs
 // its rows clamped to the last one; clamped rows are always in bounds and
 // their scores are masked.
-template <int D, int WAVES, bool CLAMP>
+template <int D, int WAVES, bool CLAMP, bool NT = true>
 __device__ __forceinline__ void tile_copy(uint8_t *ktile, uint8_t *vtile,
                                           const CopyPlan<D, WAVES> &cp, const uint16_t *skg,
                                           const uint16_t *svg, int key0, int L, int wave) {
@@ -259,11 +282,11 @@ __device__ __forceinline__ void tile_copy(uint8_t *ktile, uint8_t *vtile,
     uint8_t *dst = (is_v ? vtile : ktile) + q * 1024;
     if constexpr (!CLAMP) {
       // the tile's first row is uniform: only the lane's offset is per lane
-      dma16s(base + (int64_t)key0 * Gm::RB, cp.off[i], dst);
+      dma16s<NT>(base + (int64_t)key0 * Gm::RB, cp.off[i], dst);
     } else {
       const int row = C::row_of(cp.off[i]);
       const int key = min(key0 + row, L - 1);
-      dma16(base + (int64_t)key * Gm::RB + (cp.off[i] - (uint32_t)(row * Gm::RB)), dst);
+      dma16<NT>(base + (int64_t)key * Gm::RB + (cp.off[i] - (uint32_t)(row * Gm::RB)), dst);
     }
   }
 }
@@ -920,7 +943,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       const int qrr = min(row0 + rg * 32 + qr, p.M - 1);
       const int qb = qrr / G;
       const int64_t qro = (((int64_t)r * BW + qb) * p.Hq + k * G + (qrr - qb * G)) * D;
-      dma16(qg + qro + (((lane % Gm::SLOTS) ^ Gm::swz(qr)) << 3), qlds + n * 1024);
+      dma16<false>(qg + qro + (((lane % Gm::SLOTS) ^ Gm::swz(qr)) << 3), qlds + n * 1024);
     }
   }
 
@@ -944,7 +967,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   if (speculate) {
 #pragma unroll
     for (int i = 0; i < 3; ++i)
-      tile_copy<D, WAVES, false>(tiles + i * Gm::TILE_BYTES, tiles + (NSTAGE + i) * Gm::TILE_BYTES,
+      tile_copy<D, WAVES, false, false>(tiles + i * Gm::TILE_BYTES, tiles + (NSTAGE + i) * Gm::TILE_BYTES,
                                  cplan, skg, svg, i * KT, 0, wave);
   }
   // The prompt's tiles are split evenly over the key splits; this
@@ -965,15 +988,16 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   } else if (L < KT) {
     if (speculate) wait_vm_lgkm0<0>();  // this wave's copies into the stages have landed
     if (n_tiles > 0)
-      tile_copy<D, WAVES, true>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, 0, L, wave);
+      tile_copy<D, WAVES, true, false>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, 0, L, wave);
   } else {
     if (speculate) wait_vm_lgkm0<0>();
-    tile_copy<D, WAVES, false>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, XATTN_KEY0(0), L, wave);
+    tile_copy<D, WAVES, false, false>(XATTN_KT(0), XATTN_VT(0), cplan, skg, svg, XATTN_KEY0(0), L,
+                                      wave);
     if (n_tiles > 1)
-      tile_copy<D, WAVES, false>(XATTN_KT(1), XATTN_VT(1), cplan, skg, svg, XATTN_KEY0(1), L,
+      tile_copy<D, WAVES, false, false>(XATTN_KT(1), XATTN_VT(1), cplan, skg, svg, XATTN_KEY0(1), L,
                                  wave);
     if (n_tiles > 2)
-      tile_copy<D, WAVES, false>(XATTN_KT(2), XATTN_VT(2), cplan, skg, svg, XATTN_KEY0(2), L,
+      tile_copy<D, WAVES, false, false>(XATTN_KT(2), XATTN_VT(2), cplan, skg, svg, XATTN_KEY0(2), L,
                                  wave);
   }
 
