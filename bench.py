@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--mask-steps", type=int, default=20,
                     help="rounds of valid-path masking timed after the main run, per depth, on "
                          "the workload's beams over the full item vocabulary (0 skips it)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak leg (a 1 GiB device copy and the "
+                         "matrix-core probe)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -285,6 +288,57 @@ def valid_mask_leg(w, steps: int, dev, stream) -> dict | None:
 
 # ------------------------------------------------------------ beam selection
 
+def achievable_peaks_leg(dev, stream) -> dict:
+    """What this chip delivers: the HBM read probe over 1 GiB
+    (xattn_peak_read), a 1 GiB device-to-device copy (bytes read + written
+    per second, for context) and the matrix-core probe (xattn_peak_mfma_bf16,
+    independent bf16 MFMA chains on every SIMD), each the median of 5 timed
+    runs after 2 untimed ones."""
+    import torch
+    from generative_recommendation_beam_xattn_amd import binding as B
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = []
+    for k in range(7):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        if k >= 2:
+            t_copy.append(a.elapsed_time(b) / 1e3)
+    del dst
+    t_read = []
+    for k in range(7):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev:
+            e.record(stream)
+        B.peak_read(src, 8192, stream, ev)
+        torch.cuda.synchronize()
+        if k >= 2:
+            t_read.append(ev[0].elapsed_time(ev[1]) / 1e3)
+    del src
+    blocks, iters = 1024, 4000      # 4 waves per SIMD on 256 CUs, about 1 ms
+    t_mfma, flops = [], 0.0
+    for k in range(7):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        for e in ev:
+            e.record(stream)
+        flops, _ = B.peak_mfma_bf16(iters, blocks, stream, ev)
+        torch.cuda.synchronize()
+        if k >= 2:
+            t_mfma.append(ev[0].elapsed_time(ev[1]) / 1e3)
+    return {"hbm_read_GBps": float((1 << 30) / np.median(t_read) / 1e9),
+            "hbm_copy_GBps": float(2 * (1 << 30) / np.median(t_copy) / 1e9),
+            "mfma_bf16_TFLOPs": float(flops / np.median(t_mfma) / 1e12),
+            "read": "xattn_peak_read: 1 GiB streamed once by 8192 workgroups, 16-byte "
+                    "non-temporal loads",
+            "copy": "1 GiB device-to-device copy, bytes read + written",
+            "mfma": "xattn_peak_mfma_bf16: %d workgroups x 4 waves, %d rounds of 4 independent "
+                    "v_mfma_f32_32x32x16_bf16 chains" % (blocks, iters)}
+
+
 def beam_selection_leg(w, steps: int, dev) -> dict:
     """xattn_beam_topk on the workload's candidate pool: every beam proposes
     BW candidates (the BW x BW pools of the xGR summary), R requests per
@@ -425,6 +479,7 @@ def main():
                         2 * w.elem_bytes * w.D * w.Hkv * w.BW * int(np.sum(w.prompt_len))),
                     "steps": args.per_beam_steps}
 
+    peaks = None if args.no_peaks else achievable_peaks_leg(dev, stream)
     beam_sel = beam_selection_leg(w, args.topk_steps, dev) if args.topk_steps > 0 else None
     reorder = reorder_leg(w, copies, args.reorder_steps, stream) if args.reorder_steps > 0 else None
     masks = valid_mask_leg(w, args.mask_steps, dev, stream) if args.mask_steps > 0 else None
@@ -445,6 +500,11 @@ def main():
                 "peak": peak_c, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(w, w.dtype)
+    if peaks is not None:
+        # the same achieved rate against what this chip delivers (published
+        # peaks assume the top clock and an ideal memory system)
+        ref = {"hbm": peaks["hbm_read_GBps"], "mfma": peaks["mfma_bf16_TFLOPs"]}.get(roof["bound"])
+        peaks["roofline_frac_of_achievable"] = roof["achieved"] / ref if ref else None
 
     beam_steps = args.steps * n_calls * w.R * w.BW
     line = {
@@ -476,6 +536,7 @@ def main():
                                    "flops": flops_per_launch},
         "kernel_sha256_16": kernel_digest(w.dtype),
         "cpu_baseline": None,
+        "achievable_peaks": peaks,
         "per_beam_comparison": per_beam,
         "beam_selection": beam_sel,
         "unshared_reorder": reorder,

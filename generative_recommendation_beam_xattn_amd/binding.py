@@ -55,7 +55,8 @@ EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_de
            "xattn_resolve_ancestors", "xattn_reorder_unshared", "xattn_reorder_unshared_timed",
            "xattn_beam_topk", "xattn_beam_topk_timed", "xattn_trie_build", "xattn_valid_mask",
            "xattn_valid_mask_timed", "xattn_trie_advance",
-           "xattn_status_string", "xattn_last_error")
+           "xattn_peak_mfma_bf16", "xattn_peak_read", "xattn_status_string",
+           "xattn_last_error")
 
 
 def library_path() -> str:
@@ -106,6 +107,10 @@ def load():
         lib.xattn_valid_mask_timed.restype = ctypes.c_int
         lib.xattn_trie_advance.argtypes = [T, P, i32, P, P, i64, P, i64, P, i32, i32, P]
         lib.xattn_trie_advance.restype = ctypes.c_int
+        lib.xattn_peak_mfma_bf16.argtypes = [i32, i32, P, P, P, P, ctypes.POINTER(ctypes.c_double)]
+        lib.xattn_peak_mfma_bf16.restype = ctypes.c_int
+        lib.xattn_peak_read.argtypes = [P, i64, i32, P, P, P, P]
+        lib.xattn_peak_read.restype = ctypes.c_int
         lib.xattn_status_string.argtypes = [ctypes.c_int]
         lib.xattn_status_string.restype = ctypes.c_char_p
         lib.xattn_last_error.argtypes = []
@@ -421,6 +426,30 @@ def beam_topk(cum, logp, token, out=None, stream=None, events=None):
     else:
         st = lib.xattn_beam_topk_timed(*args, _event(events[0]), _event(events[1]))
     _check(st)
+    return out
+
+
+def peak_mfma_bf16(iters: int, blocks: int, stream=None, events=None, device="cuda"):
+    """Matrix-core throughput probe (xattn_peak_mfma_bf16).  Returns the
+    floating-point operations of the launch; with events (a recorded
+    (start, stop) torch.cuda.Event pair) the dispatch is timed."""
+    lib = load()
+    out = torch.empty(int(blocks) * 256, dtype=torch.float32, device=device)
+    flops = ctypes.c_double(0.0)
+    ev = (None, None) if events is None else (_event(events[0]), _event(events[1]))
+    _check(lib.xattn_peak_mfma_bf16(int(iters), int(blocks), _ptr(out),
+                                    _stream(stream, out.device), ev[0], ev[1],
+                                    ctypes.byref(flops)))
+    return flops.value, out
+
+
+def peak_read(src, blocks: int, stream=None, events=None):
+    """HBM read probe (xattn_peak_read) over the bytes of tensor src."""
+    lib = load()
+    out = torch.empty(int(blocks) * 256, dtype=torch.int32, device=src.device)
+    ev = (None, None) if events is None else (_event(events[0]), _event(events[1]))
+    _check(lib.xattn_peak_read(_ptr(src), src.numel() * src.element_size(), int(blocks),
+                               _ptr(out), _stream(stream, src.device), ev[0], ev[1]))
     return out
 
 

@@ -539,4 +539,39 @@ const char *xattn_status_string(xattn_status status) {
 
 const char *xattn_last_error(void) { return g_last_error; }
 
+xattn_status xattn_peak_mfma_bf16(int32_t iters, int32_t blocks, float *out, void *stream,
+                                  void *start_event, void *stop_event, double *flops) {
+  if (iters < 1 || blocks < 1) return fail(XATTN_EINVAL, "iters and blocks must be >= 1");
+  if (!out || !aligned(out, 4)) return fail(XATTN_EINVAL, "out must be a 4-byte-aligned device buffer");
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(XATTN_EINVAL, "give both timing events or neither");
+  xattn::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  const hipError_t e =
+      xattn::launch_peak_mfma(iters, blocks, out, static_cast<hipStream_t>(stream), ev);
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  if (flops) *flops = xattn::peak_mfma_flops(iters, blocks);
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
+xattn_status xattn_peak_read(const void *src, int64_t bytes, int32_t blocks, uint32_t *out,
+                             void *stream, void *start_event, void *stop_event) {
+  if (blocks < 1 || bytes < 16 || bytes % 16 != 0)
+    return fail(XATTN_EINVAL, "blocks must be >= 1 and bytes a positive multiple of 16");
+  if (!src || !aligned(src, 16)) return fail(XATTN_EINVAL, "src must be a 16-byte-aligned device buffer");
+  if (!out || !aligned(out, 4)) return fail(XATTN_EINVAL, "out must be a 4-byte-aligned device buffer");
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(XATTN_EINVAL, "give both timing events or neither");
+  xattn::LaunchEvents ev;
+  ev.start = static_cast<hipEvent_t>(start_event);
+  ev.stop = static_cast<hipEvent_t>(stop_event);
+  const hipError_t e =
+      xattn::launch_peak_read(src, bytes, blocks, out, static_cast<hipStream_t>(stream), ev);
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  g_last_error[0] = '\0';
+  return XATTN_OK;
+}
+
 }  // extern "C"

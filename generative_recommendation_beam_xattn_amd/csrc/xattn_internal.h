@@ -88,6 +88,18 @@ hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream
 // Unshared stage alone for deep chains (p.anc resolved): per query row its
 // partial (m, l) into p.tok_ml and unnormalised o into p.tok_o, in the units
 // of the staged kernel's online softmax (raw scores, exp2 with scale_log2).
+// Matrix-core throughput probe (measurement only): blocks workgroups of
+// kPeakThreads threads, iters rounds of independent bf16 MFMAs per wave;
+// out receives one float per thread.
+constexpr int kPeakThreads = 256;
+double peak_mfma_flops(int32_t iters, int32_t blocks);
+hipError_t launch_peak_mfma(int32_t iters, int32_t blocks, float *out, hipStream_t stream,
+                            LaunchEvents ev);
+// HBM read probe: blocks workgroups stream the 16-byte units of src;
+// out receives one word per thread.
+hipError_t launch_peak_read(const void *src, int64_t bytes, int32_t blocks, uint32_t *out,
+                            hipStream_t stream, LaunchEvents ev);
+
 hipError_t launch_token_partials_bf16(const DecodeParams &p, hipStream_t stream,
                                       LaunchEvents ev = {});
 
