@@ -1,0 +1,60 @@
+"""The benchmark's algorithmic work per call, against independent counts.
+
+Unique-KV bytes count every prompt row once per (request, KV head) and every
+distinct generated-token (level, slot) row that some beam's history reaches
+once, for K and V.  Here the distinct rows come from beam histories
+simulated forward by copying (tests/brute.py), not from the backward walk
+the benchmark uses; FLOPs are summed query row by query row.
+"""
+import numpy as np
+import pytest
+
+import bench
+from generative_recommendation_beam_xattn_amd import workloads as W
+from tests.brute import histories
+
+
+def distinct_rows_forward(parent_idx_r, step):
+    """parent_idx_r: one request's [S][BW] parent rows."""
+    hist = histories(parent_idx_r[None], step)[0]
+    return len({pair for h in hist for pair in h})
+
+
+@pytest.mark.parametrize("seed,BW,step,kind", [(0, 4, 0, "uniform"), (1, 6, 3, "uniform"),
+                                               (2, 16, 5, "uniform"), (3, 32, 2, "skewed"),
+                                               (4, 8, 7, "identity")])
+def test_distinct_ancestor_rows_match_forward_histories(seed, BW, step, kind):
+    w = W.custom(seed=seed, R=3, L=5, BW=BW, steps=[step], Hq=2, Hkv=1, D=64, dtype="f32",
+                 parents=kind)
+    for r in range(w.R):
+        assert bench.distinct_ancestor_rows(w.parent_idx[r], step) == \
+            distinct_rows_forward(w.parent_idx[r], step)
+
+
+def test_identity_parents_reach_every_row_and_constant_rows_one():
+    BW, S = 5, 4
+    ident = np.tile(np.arange(BW, dtype=np.int32), (S, 1))
+    assert bench.distinct_ancestor_rows(ident, S - 1) == BW * S
+    const = np.zeros((S, BW), np.int32)   # every beam descends from slot 0
+    assert bench.distinct_ancestor_rows(const, S - 1) == BW + (S - 1)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_algorithmic_work_row_by_row(dtype):
+    w = W.custom(seed=7, R=3, L=[10, 0, 33], BW=5, steps=[0, 2], Hq=6, Hkv=2, D=64,
+                 dtype=dtype, S=3)
+    e = 2 if dtype == "bf16" else 4
+    for i, s in enumerate(w.steps):
+        work = bench.algorithmic_work(w, i)
+        flops = 0
+        kv_rows = 0
+        for r in range(w.R):
+            L = int(w.prompt_len[r])
+            for b in range(w.BW):
+                for h in range(w.Hq):
+                    flops += 4 * w.D * (L + s + 1)   # q.k and p.v per key
+            kv_rows += w.Hkv * (L + distinct_rows_forward(w.parent_idx[r], s))
+        assert work["flops"] == flops
+        assert work["unique_kv_bytes"] == 2 * kv_rows * w.D * e
+        q_bytes = w.R * w.BW * w.Hq * w.D * e
+        assert work["bytes"] == work["unique_kv_bytes"] + 2 * q_bytes + work["index_bytes"]
