@@ -4,12 +4,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--G g]
 
 One benchmark step is one pass of the whole path over one batch of the
-workload: for the default GR-serving workload (16 requests, prompt lengths
-uniform in [512, 1024], 128 beams, 3 decode steps, 16 query / 4 KV heads,
-head_dim 128, bf16) that is 3 calls of xattn_decode, levels 0, 1, 2.  Inputs
-are resident in HBM before timing starts; enough distinct copies of them are
-rotated (>= 1 GB) that timed calls read HBM rather than the 256 MB Infinity
-Cache.
+workload: for the default large-batch workload (64 requests, 2048-token
+prompts, 256 beams with skewed branching, 3 decode steps, 32 query / 8 KV
+heads, head_dim 128, bf16) that is 3 calls of xattn_decode, levels 0, 1, 2.
+Inputs are resident in HBM before timing starts; enough distinct copies of
+them are rotated (>= 1 GB) that timed calls read HBM rather than the 256 MB
+Infinity Cache.
 
 Prints ONE JSON line.  `value` is beam-steps per second over the timed
 region (wall clock between two device synchronisations).  `roofline` covers
@@ -21,8 +21,10 @@ are bound to the calls of every n-th step of the timed region (--time-every,
 default 4): their markers cost the GPU about 4 us per launch, which binding
 them to every call would charge to the throughput.
 `cpu_baseline` times the float64 CPU oracle on the host cores on a bounded
-sample of the same workload.  After the timed region, two side legs time
-other kernels on the same device: `per_beam_comparison` (the per-beam
+sample of the same workload.  After the timed region, `other_workloads`
+measures the other workloads the same way with fewer steps (GR serving,
+wide beam, and the prefix-homogeneity sweep at every group size), and side
+legs time other kernels on the same device: `per_beam_comparison` (the per-beam
 PagedAttention-style kernel on the same inputs), `beam_selection` (the
 top-BW beam selection on the workload's BW x BW candidate pool),
 `unshared_reorder` (the in-place Unshared-cache reorder at each level) and
@@ -48,8 +50,14 @@ METRIC = "decode-attention beam-steps/sec + achieved HBM GB/s (unique KV bytes) 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 FP32_VECTOR_PEAK_TFLOPS = 157.3
-KERNEL_SOURCES = {"bf16": "generative_recommendation_beam_xattn_amd/csrc/kernel_bf16_mfma.hip",
-                  "f32": "generative_recommendation_beam_xattn_amd/csrc/kernel_f32.hip"}
+# everything that decides the device code: the HIP sources, the headers and
+# the build flags
+CODE_GLOBS = ("generative_recommendation_beam_xattn_amd/csrc/*", "include/*.h",
+              "generative_recommendation_beam_xattn_amd/build.py")
+# what the main line measures when no --config is given: the largest
+# single-GPU workload (64 requests x 256 beams, 2048-token prompts)
+DEFAULT_CONFIG = 3
+SIDE_WORKLOADS = [(2, None), (4, None), (5, 1), (5, 8), (5, 32), (5, 256)]
 
 
 def parse():
@@ -57,7 +65,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--G", type=int, default=None, help="prefix group size for config 5")
     ap.add_argument("--rot", type=int, default=None, help="rotation copies (default: >= 1 GB)")
     ap.add_argument("--time-every", type=int, default=4,
@@ -84,6 +92,8 @@ def parse():
                          "matrix-core probe)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--side-steps", type=int, default=40,
+                    help="timed steps of each other workload (0 skips them)")
     return ap.parse_args()
 
 
@@ -130,21 +140,39 @@ def workload_config(w, n_rot: int) -> dict:
     return c
 
 
-def kernel_digest(dtype: str) -> str:
-    with open(os.path.join(ROOT, KERNEL_SOURCES[dtype]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def code_digest() -> str:
+    """Digest of every file that decides the device code (sources, headers,
+    build flags), in path order."""
+    import glob
+    h = hashlib.sha256()
+    for pattern in CODE_GLOBS:
+        for path in sorted(glob.glob(os.path.join(ROOT, pattern))):
+            if path.endswith((".hip", ".h", ".py")):
+                h.update(os.path.relpath(path, ROOT).encode())
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def stored_traffic(w, dtype: str):
-    """Counter-measured HBM bytes per launch, if taken on the current kernel."""
+def stored_traffic(w):
+    """Counter-measured HBM bytes per launch (profiles/traffic_<workload>.json,
+    FETCH_SIZE + WRITE_SIZE scaled by a copy of known size), or None unless
+    they were taken on exactly the current device code."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_sha256_16") != kernel_digest(dtype):
+    if rec.get("code_sha256_16") != code_digest():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def data_label(w) -> str:
+    c = w.meta.get("config")
+    kind = {1: "tiny plumbing", 2: "GR serving", 3: "large batch", 4: "wide beam",
+            5: "prefix-homogeneity sweep"}.get(c, w.name)
+    return "synthetic (seeded N(0,1), %s workload shape: %s)" % (kind, w.name)
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -382,6 +410,152 @@ def beam_selection_leg(w, steps: int, dev) -> dict:
 
 # ---------------------------------------------------------------------- main
 
+def roofline_of(w, work, t_kernel: float) -> dict:
+    """The binding roofline of one launch: algorithmic bytes (HBM) or FLOPs
+    (matrix cores) per launch over the mean launch duration."""
+    bytes_per_launch = float(np.mean([x["bytes"] for x in work]))
+    flops_per_launch = float(np.mean([x["flops"] for x in work]))
+    t_hbm = bytes_per_launch / (HBM_PEAK_GBS * 1e9)
+    peak_c = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+    t_cmp = flops_per_launch / (peak_c * 1e12)
+    if t_hbm >= t_cmp:
+        roof = {"bound": "hbm", "achieved": bytes_per_launch / t_kernel / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                "achieved": flops_per_launch / t_kernel / 1e12, "peak": peak_c,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["binding_frac"] = max(t_hbm, t_cmp) / t_kernel
+    return roof
+
+
+class Measured:
+    """One workload on the device: rotation copies of every input, decode
+    calls marshalled once, a timed region of whole steps (all decode levels
+    of the workload) between two synchronisations, and each call's kernel
+    duration from events bound to its dispatch on every n-th step."""
+
+    def __init__(self, w, dev, rot=None):
+        import torch
+        from generative_recommendation_beam_xattn_amd import binding as B
+
+        def to_dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        self.w = w
+        self.n_calls = len(w.steps)
+        self.work = [algorithmic_work(w, i) for i in range(self.n_calls)]
+        copy_bytes = (w.q.nbytes * 2 + w.shared_k.nbytes * 2 + w.unshared_k.nbytes * 2 +
+                      w.parent_idx.nbytes)
+        self.n_rot = rot or max(1, min(32, math.ceil(1e9 / copy_bytes)))
+        base = {"q": [to_dev(w.q[i]) for i in range(self.n_calls)], "sk": to_dev(w.shared_k),
+                "sv": to_dev(w.shared_v), "pl": to_dev(w.prompt_len),
+                "uk": to_dev(w.unshared_k), "uv": to_dev(w.unshared_v),
+                "par": to_dev(w.parent_idx)}
+        self.copies = [base] + [{k: ([t.clone() for t in v] if isinstance(v, list)
+                                     else v.clone()) for k, v in base.items()}
+                                for _ in range(self.n_rot - 1)]
+        self.calls = [[B.PreparedDecode(c["q"][i], c["sk"], c["sv"], c["pl"], c["uk"], c["uv"],
+                                        c["par"], w.steps[i]) for i in range(self.n_calls)]
+                      for c in self.copies]
+
+    def run(self, stream, steps: int, warmup: int, every: int):
+        import torch
+        n_calls, n_rot = self.n_calls, self.n_rot
+
+        def run_step(k, events=None):
+            for i, call in enumerate(self.calls[k % n_rot]):
+                call(stream, None if events is None else (events[2 * i], events[2 * i + 1]))
+
+        for k in range(warmup):
+            run_step(k)
+        timed_steps = [k for k in range(steps) if k % every == 0]
+        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
+              for k in timed_steps}
+        for row in ev.values():   # torch creates the HIP event at its first record
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            run_step(warmup + k, ev.get(k))
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - t0
+        self.steps = steps
+        # per-launch durations (ms) of each decode call, by level
+        self.per_call = np.array([[ev[k][2 * i].elapsed_time(ev[k][2 * i + 1])
+                                   for i in range(n_calls)] for k in timed_steps])
+        self.every = every
+        return self
+
+    def summary(self, with_traffic=True) -> dict:
+        w = self.w
+        mean_launch_s = self.per_call.mean(axis=0) / 1e3
+        t_kernel = float(mean_launch_s.mean())
+        roof = roofline_of(w, self.work, t_kernel)
+        binding = roof.pop("binding_frac")
+        roof["traffic"] = stored_traffic(w) if with_traffic else None
+        ukv = float(np.mean([x["unique_kv_bytes"] for x in self.work]))
+        rows = self.steps * self.n_calls * w.R * w.BW
+        return {
+            "value": rows / self.wall,
+            "unit": "sequence-steps/s" if w.meta.get("config") == 5 else "beam-steps/s",
+            "ms_per_step": self.wall / self.steps * 1e3,
+            "steps": self.steps,
+            "dtype": w.dtype,
+            "data": data_label(w),
+            "config": workload_config(w, self.n_rot),
+            "roofline": roof,
+            "unique_kv_GBps": ukv / t_kernel / 1e9,
+            "unique_kv_frac_of_hbm_peak": ukv / t_kernel / 1e9 / HBM_PEAK_GBS,
+            "binding_roofline_frac": binding,
+            "kernel_us_per_launch": {"mean": t_kernel * 1e6,
+                                     "by_level": [float(x * 1e6) for x in mean_launch_s],
+                                     "p10": float(np.percentile(self.per_call, 10) * 1e3),
+                                     "p50": float(np.percentile(self.per_call, 50) * 1e3),
+                                     "p90": float(np.percentile(self.per_call, 90) * 1e3),
+                                     "launches_timed": int(self.per_call.size),
+                                     "every_nth_step": self.every},
+            "algorithmic_per_launch": {
+                "bytes": float(np.mean([x["bytes"] for x in self.work])),
+                "unique_kv_bytes": ukv,
+                "flops": float(np.mean([x["flops"] for x in self.work]))},
+        }
+
+
+def per_beam_leg(m, stream, steps: int) -> dict:
+    """The per-beam (PagedAttention-style) comparison kernel on the same
+    inputs, outside the timed region: its per-launch duration, as the staged
+    one's."""
+    import torch
+    from generative_recommendation_beam_xattn_amd import binding as B
+    w = m.w
+    pb_calls = [[B.PreparedDecode(c["q"][i], c["sk"], c["sv"], c["pl"], c["uk"], c["uv"],
+                                  c["par"], w.steps[i], per_beam=True)
+                 for i in range(m.n_calls)] for c in m.copies]
+    pb_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * m.n_calls)]
+             for _ in range(steps + 1)]
+    for row in pb_ev:
+        for e in row:
+            e.record(stream)
+    for k in range(steps + 1):   # the first step is a warmup
+        for i, call in enumerate(pb_calls[k % m.n_rot]):
+            call(stream, (pb_ev[k][2 * i], pb_ev[k][2 * i + 1]))
+    torch.cuda.synchronize()
+    pb = np.array([[pb_ev[k][2 * i].elapsed_time(pb_ev[k][2 * i + 1]) for i in range(m.n_calls)]
+                   for k in range(1, steps + 1)])
+    pb_us = float(pb.mean() * 1e3)
+    return {"kernel_us_per_launch": pb_us,
+            "staged_speedup": pb_us / (float(m.per_call.mean()) * 1e3),
+            "prompt_bytes_read_per_launch": float(
+                2 * w.elem_bytes * w.D * w.Hkv * w.BW * int(np.sum(w.prompt_len))),
+            "steps": steps}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -391,55 +565,15 @@ def main():
         sys.exit(2)
 
     import torch
-    from generative_recommendation_beam_xattn_amd import binding as B
     from generative_recommendation_beam_xattn_amd import workloads as W
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    def to_dev(a):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    every = max(1, args.time_every)
 
     w = W.make(args.config, args.G)
-    n_calls = len(w.steps)
-    work = [algorithmic_work(w, i) for i in range(n_calls)]
-    copy_bytes = (w.q.nbytes * 2 + w.shared_k.nbytes * 2 + w.unshared_k.nbytes * 2 +
-                  w.parent_idx.nbytes)
-    n_rot = args.rot or max(1, min(32, math.ceil(1e9 / copy_bytes)))
-
-    # rotation copies of every input (and output) resident in HBM
-    base = {"q": [to_dev(w.q[i]) for i in range(n_calls)], "sk": to_dev(w.shared_k),
-            "sv": to_dev(w.shared_v), "pl": to_dev(w.prompt_len), "uk": to_dev(w.unshared_k),
-            "uv": to_dev(w.unshared_v), "par": to_dev(w.parent_idx)}
-    copies = [base] + [{k: ([t.clone() for t in v] if isinstance(v, list) else v.clone())
-                        for k, v in base.items()} for _ in range(n_rot - 1)]
-    calls = [[B.PreparedDecode(c["q"][i], c["sk"], c["sv"], c["pl"], c["uk"], c["uv"], c["par"],
-                               w.steps[i]) for i in range(n_calls)] for c in copies]
-    stream = torch.cuda.current_stream(dev)
-
-    def run_step(k, events=None):
-        for i, call in enumerate(calls[k % n_rot]):
-            call(stream, None if events is None else (events[2 * i], events[2 * i + 1]))
-
-    for k in range(args.warmup):
-        run_step(k)
-    every = max(1, args.time_every)
-    timed_steps = [k for k in range(args.steps) if k % every == 0]
-    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
-          for k in timed_steps}
-    for row in ev.values():   # torch creates the HIP event at its first record
-        for e in row:
-            e.record(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        run_step(args.warmup + k, ev.get(k))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
+    m = Measured(w, dev, args.rot).run(stream, args.steps, args.warmup, every)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -448,96 +582,66 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    # per-launch durations (ms) of each decode call, by level
-    per_call = np.array([[ev[k][2 * i].elapsed_time(ev[k][2 * i + 1]) for i in range(n_calls)]
-                         for k in timed_steps])
-    mean_launch_s = per_call.mean(axis=0) / 1e3
-
-    # the per-beam (PagedAttention-style) comparison kernel on the same inputs,
-    # outside the timed region: its per-launch duration, as the staged one's
-    per_beam = None
-    if args.per_beam_steps > 0:
-        pb_calls = [[B.PreparedDecode(c["q"][i], c["sk"], c["sv"], c["pl"], c["uk"], c["uv"],
-                                      c["par"], w.steps[i], per_beam=True)
-                     for i in range(n_calls)] for c in copies]
-        pb_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls)]
-                 for _ in range(args.per_beam_steps + 1)]
-        for row in pb_ev:
-            for e in row:
-                e.record(stream)
-        for k in range(args.per_beam_steps + 1):   # the first step is a warmup
-            for i, call in enumerate(pb_calls[k % n_rot]):
-                call(stream, (pb_ev[k][2 * i], pb_ev[k][2 * i + 1]))
-        torch.cuda.synchronize()
-        pb = np.array([[pb_ev[k][2 * i].elapsed_time(pb_ev[k][2 * i + 1]) for i in range(n_calls)]
-                       for k in range(1, args.per_beam_steps + 1)])
-        pb_us = float(pb.mean() * 1e3)
-        per_beam = {"kernel_us_per_launch": pb_us,
-                    "staged_speedup": pb_us / (float(per_call.mean()) * 1e3),
-                    "prompt_bytes_read_per_launch": float(
-                        2 * w.elem_bytes * w.D * w.Hkv * w.BW * int(np.sum(w.prompt_len))),
-                    "steps": args.per_beam_steps}
-
+    per_beam = per_beam_leg(m, stream, args.per_beam_steps) if args.per_beam_steps > 0 else None
     peaks = None if args.no_peaks else achievable_peaks_leg(dev, stream)
     beam_sel = beam_selection_leg(w, args.topk_steps, dev) if args.topk_steps > 0 else None
-    reorder = reorder_leg(w, copies, args.reorder_steps, stream) if args.reorder_steps > 0 else None
+    reorder = (reorder_leg(w, m.copies, args.reorder_steps, stream)
+               if args.reorder_steps > 0 else None)
     masks = valid_mask_leg(w, args.mask_steps, dev, stream) if args.mask_steps > 0 else None
 
-    t_kernel = float(mean_launch_s.mean())
-    bytes_per_launch = float(np.mean([x["bytes"] for x in work]))
-    flops_per_launch = float(np.mean([x["flops"] for x in work]))
-    ukv_per_launch = float(np.mean([x["unique_kv_bytes"] for x in work]))
-    t_hbm = bytes_per_launch / (HBM_PEAK_GBS * 1e9)
-    peak_c = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
-    t_cmp = flops_per_launch / (peak_c * 1e12)
-    if t_hbm >= t_cmp:
-        achieved = bytes_per_launch / t_kernel / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    else:
-        achieved = flops_per_launch / t_kernel / 1e12
-        roof = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved,
-                "peak": peak_c, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(w, w.dtype)
+    head = m.summary()
     if peaks is not None:
         # the same achieved rate against what this chip delivers (published
         # peaks assume the top clock and an ideal memory system)
+        roof = head["roofline"]
         ref = {"hbm": peaks["hbm_read_GBps"], "mfma": peaks["mfma_bf16_TFLOPs"]}.get(roof["bound"])
         peaks["roofline_frac_of_achievable"] = roof["achieved"] / ref if ref else None
+    del m
+    torch.cuda.empty_cache()
 
-    beam_steps = args.steps * n_calls * w.R * w.BW
+    # the other workloads, each measured the same way on fewer steps
+    others = []
+    if args.side_steps > 0:
+        for cfg, G in SIDE_WORKLOADS:
+            if (cfg, G) == (args.config, args.G):
+                continue
+            ws = W.make(cfg, G)
+            ms = Measured(ws, dev).run(stream, args.side_steps, max(5, args.side_steps // 4), every)
+            sm = ms.summary()
+            if per_beam is not None and cfg != 5:
+                sm["per_beam_comparison"] = per_beam_leg(ms, stream, 3)
+            others.append(sm)
+            del ms, ws
+            torch.cuda.empty_cache()
+            print("bench: %s done" % sm["config"]["workload"], file=sys.stderr, flush=True)
+
     line = {
         "metric": METRIC,
-        "value": beam_steps / wall,
-        "unit": "beam-steps/s",
+        "value": head["value"],
+        "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1), workload shape of the GR serving configuration)",
-        "config": workload_config(w, n_rot),
-        "roofline": roof,
-        "unique_kv_GBps": ukv_per_launch / t_kernel / 1e9,
-        "unique_kv_frac_of_hbm_peak": ukv_per_launch / t_kernel / 1e9 / HBM_PEAK_GBS,
-        "binding_roofline_frac": max(t_hbm, t_cmp) / t_kernel,
-        "kernel_us_per_launch": {"mean": t_kernel * 1e6,
-                                 "by_level": [float(x * 1e6) for x in mean_launch_s],
-                                 "p10": float(np.percentile(per_call, 10) * 1e3),
-                                 "p50": float(np.percentile(per_call, 50) * 1e3),
-                                 "p90": float(np.percentile(per_call, 90) * 1e3),
-                                 "launches_timed": int(per_call.size),
-                                 "every_nth_step": every},
-        "algorithmic_per_launch": {"bytes": bytes_per_launch, "unique_kv_bytes": ukv_per_launch,
-                                   "flops": flops_per_launch},
-        "kernel_sha256_16": kernel_digest(w.dtype),
+        "dtype": head["dtype"],
+        "data": head["data"],
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "unique_kv_GBps": head["unique_kv_GBps"],
+        "unique_kv_frac_of_hbm_peak": head["unique_kv_frac_of_hbm_peak"],
+        "binding_roofline_frac": head["binding_roofline_frac"],
+        "kernel_us_per_launch": head["kernel_us_per_launch"],
+        "algorithmic_per_launch": head["algorithmic_per_launch"],
+        "code_sha256_16": code_digest(),
         "cpu_baseline": None,
         "achievable_peaks": peaks,
         "per_beam_comparison": per_beam,
+        "other_workloads": others,
         "beam_selection": beam_sel,
         "unshared_reorder": reorder,
         "valid_path_mask": masks,

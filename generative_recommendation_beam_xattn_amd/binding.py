@@ -42,6 +42,22 @@ class Trie(ctypes.Structure):
                 ("total_bytes", ctypes.c_int64)]
 
 
+class Plan(ctypes.Structure):
+    """xattn_plan (include/xattn.h): what one xattn_decode call enqueues."""
+    _fields_ = [("kernel", ctypes.c_int32), ("kernels", ctypes.c_int32),
+                ("ancestor_walk", ctypes.c_int32), ("unshared_kernel", ctypes.c_int32),
+                ("key_splits", ctypes.c_int32), ("rows_per_block", ctypes.c_int32),
+                ("threads_per_block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("parents_in_lds", ctypes.c_int32), ("beams_per_block", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+KERNEL_STAGED_BF16, KERNEL_F32, KERNEL_PER_BEAM_BF16 = 0, 1, 2
+
+
 class Shape(ctypes.Structure):
     _fields_ = [("num_requests", ctypes.c_int32), ("beam_width", ctypes.c_int32),
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
@@ -50,7 +66,8 @@ class Shape(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
-EXPORTS = ("xattn_decode", "xattn_decode_debug", "xattn_decode_timed", "xattn_decode_per_beam",
+EXPORTS = ("xattn_decode", "xattn_decode_with_ancestors", "xattn_plan_decode",
+           "xattn_decode_debug", "xattn_decode_timed", "xattn_decode_per_beam",
            "xattn_decode_per_beam_timed", "xattn_workspace_size",
            "xattn_resolve_ancestors", "xattn_reorder_unshared", "xattn_reorder_unshared_timed",
            "xattn_beam_topk", "xattn_beam_topk_timed", "xattn_trie_build", "xattn_valid_mask",
@@ -77,6 +94,10 @@ def load():
         i32, sz = ctypes.c_int32, ctypes.c_size_t
         lib.xattn_decode.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P]
         lib.xattn_decode.restype = ctypes.c_int
+        lib.xattn_decode_with_ancestors.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, P, sz, P]
+        lib.xattn_decode_with_ancestors.restype = ctypes.c_int
+        lib.xattn_plan_decode.argtypes = [S, i32, ctypes.POINTER(Plan)]
+        lib.xattn_plan_decode.restype = ctypes.c_int
         lib.xattn_decode_debug.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, P, P, P, sz, P]
         lib.xattn_decode_debug.restype = ctypes.c_int
         lib.xattn_decode_timed.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P, P, P]
@@ -221,6 +242,32 @@ def decode(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx
                             _ptr(parent_idx), int(step), _ptr(out), _ptr(ws), ws_bytes,
                             _stream(stream, q.device)))
     return out
+
+
+def decode_with_ancestors(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx,
+                          step, out=None, workspace=None, scale: float = 0.0, stream=None):
+    """decode, and the ancestor slots the call's own chain walk used:
+    returns (out, anc) with anc int32 [R][step+1][BW] (xattn_decode_with_ancestors)."""
+    lib = load()
+    _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
+    shape = make_shape(q, shared_k, unshared_k, scale)
+    R, BW = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    anc = torch.empty((R, int(step) + 1, BW), dtype=torch.int32, device=q.device)
+    ws, ws_bytes = _workspace(shape, step, workspace, q.device)
+    _check(lib.xattn_decode_with_ancestors(
+        ctypes.byref(shape), _ptr(q), _ptr(shared_k), _ptr(shared_v), _ptr(prompt_len),
+        _ptr(unshared_k), _ptr(unshared_v), _ptr(parent_idx), int(step), _ptr(out), _ptr(anc),
+        _ptr(ws), ws_bytes, _stream(stream, q.device)))
+    return out, anc
+
+
+def plan(shape: Shape, step: int) -> Plan:
+    """xattn_plan_decode: the kernels one decode call enqueues (host only)."""
+    pl = Plan()
+    _check(load().xattn_plan_decode(ctypes.byref(shape), int(step), ctypes.byref(pl)))
+    return pl
 
 
 def decode_per_beam(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,

@@ -8,6 +8,7 @@
 #include <algorithm>
 
 #include "../../include/xattn.h"
+#include "../../include/xattn_measure.h"
 #include "../../include/xbeam.h"
 #include "xattn_internal.h"
 
@@ -114,15 +115,89 @@ size_t workspace_bytes_for(const xattn_shape *s, int32_t step) {
   return bytes;
 }
 
-xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, const void *shared_v,
-                 const int32_t *prompt_len, const void *unshared_k, const void *unshared_v,
-                 const int32_t *parent_idx, int32_t step, void *out, float *lse,
-                 float *stage_ml, float *stage_o, bool taps, void *workspace,
-                 size_t workspace_bytes, void *stream, xattn::LaunchEvents ev = {},
-                 bool per_beam = false) {
+// What one decode call enqueues for this shape and step (xattn_plan in
+// include/xattn.h): the plan the dispatch below follows, computed on the
+// host alone.
+enum Walk { kWalkInKernel = 0, kWalkChunked = 1, kWalkSegmented = 2 };
+
+xattn_status make_plan(const xattn_shape *s, int32_t step, bool per_beam, bool taps,
+                       xattn_plan *pl) {
   xattn_status st = check_shape(s, step);
   if (st != XATTN_OK) return st;
-  if (!q || !prompt_len || !unshared_k || !unshared_v || !parent_idx || !out)
+  memset(pl, 0, sizeof *pl);
+  const bool deep = deep_chain(step);
+  const int64_t G = s->num_q_heads / s->num_kv_heads;
+  const int64_t M = (int64_t)s->beam_width * G;
+  const bool staged_bf16 =
+      s->dtype == XATTN_BF16 && !per_beam && (taps || M > xattn::kPerBeamMaxRows);
+  pl->workspace_bytes = workspace_bytes_for(s, step);
+  pl->ancestor_walk = !deep ? kWalkInKernel
+                            : (seg_map_bytes_for(s, step) > 0 ? kWalkSegmented : kWalkChunked);
+  pl->kernel = s->dtype == XATTN_F32 ? XATTN_KERNEL_F32
+                                     : (staged_bf16 ? XATTN_KERNEL_STAGED_BF16
+                                                    : XATTN_KERNEL_PER_BEAM_BF16);
+  pl->key_splits = staged_bf16 && !taps ? key_splits_for(s, step) : 1;
+  pl->unshared_kernel = deep && staged_bf16 ? 1 : 0;
+  pl->kernels = (pl->ancestor_walk == kWalkSegmented ? 2 : (deep ? 1 : 0)) +
+                pl->unshared_kernel + 1 + (pl->key_splits > 1 ? 1 : 0);
+  if (staged_bf16) {
+    xattn::DecodeParams p{};
+    p.R = s->num_requests;
+    p.BW = s->beam_width;
+    p.Hq = s->num_q_heads;
+    p.Hkv = s->num_kv_heads;
+    p.D = s->head_dim;
+    p.step = step;
+    p.G = (int32_t)G;
+    p.M = (int32_t)M;
+    p.n_split = pl->key_splits;
+    static const int32_t resolved = 0;   // any non-null: slots come from the workspace
+    p.anc = deep ? &resolved : nullptr;
+    const xattn::Bf16Geometry g = xattn::bf16_geometry(p);
+    pl->rows_per_block = g.rows;
+    pl->threads_per_block = g.threads;
+    pl->grid = g.grid;
+    pl->lds_bytes = g.static_lds + g.dyn_lds;
+    pl->parents_in_lds = g.stage_par ? 1 : 0;
+    pl->beams_per_block = deep ? 0 : g.beams_per_block;
+  } else if (s->dtype == XATTN_F32) {
+    pl->rows_per_block = 1;
+    pl->threads_per_block = xattn::kF32Threads;
+    pl->grid = (int64_t)s->num_requests * s->beam_width * s->num_q_heads;
+    pl->lds_bytes = xattn::f32_lds_bytes(s->head_dim);
+  } else {
+    pl->rows_per_block = (int32_t)G;
+    pl->threads_per_block = xattn::kPerBeamThreads;
+    pl->grid = (int64_t)s->num_requests * s->beam_width * s->num_kv_heads;
+    pl->lds_bytes = xattn::per_beam_lds_bytes(s->head_dim);
+  }
+  if (pl->grid > 0x7fffffff) return fail(XATTN_EUNSUPPORTED, "too many workgroups for one launch");
+  if (pl->lds_bytes > xattn::kLdsLimit)
+    return fail(XATTN_EUNSUPPORTED, "the kernel's LDS does not fit this shape");
+  return XATTN_OK;
+}
+
+// Optional outputs and modes of one decode call.
+struct RunOpts {
+  float *lse = nullptr;          // debug taps
+  float *stage_ml = nullptr;
+  float *stage_o = nullptr;
+  int32_t *anc_out = nullptr;    // ancestor slots [R][step+1][BW]
+  bool want_anc = false;         // anc_out is a required argument
+  bool taps = false;             // debug entry: stages kept apart
+  bool per_beam = false;         // the per-beam comparison kernel
+  xattn::LaunchEvents ev{};
+};
+
+xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, const void *shared_v,
+                 const int32_t *prompt_len, const void *unshared_k, const void *unshared_v,
+                 const int32_t *parent_idx, int32_t step, void *out, void *workspace,
+                 size_t workspace_bytes, void *stream, const RunOpts &o) {
+  xattn_plan pl;
+  xattn_status st = make_plan(s, step, o.per_beam, o.taps, &pl);
+  if (st != XATTN_OK) return st;
+  if (!q || !prompt_len || !unshared_k || !unshared_v || !parent_idx || !out ||
+      (o.want_anc && !o.anc_out))
     return fail(XATTN_EINVAL, "a required pointer is NULL");
   if (s->max_prompt_len > 0 && (!shared_k || !shared_v))
     return fail(XATTN_EINVAL, "shared_k/shared_v are NULL but max_prompt_len > 0");
@@ -131,10 +206,10 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
     if (!aligned(v, 16)) return fail(XATTN_EINVAL, "q, k, v and out must be 16-byte aligned");
   if (!aligned(prompt_len, 4) || !aligned(parent_idx, 4))
     return fail(XATTN_EINVAL, "int32 arrays must be 4-byte aligned");
-  if ((lse && !aligned(lse, 4)) || (stage_ml && !aligned(stage_ml, 4)) ||
-      (stage_o && !aligned(stage_o, 4)))
+  if ((o.lse && !aligned(o.lse, 4)) || (o.stage_ml && !aligned(o.stage_ml, 4)) ||
+      (o.stage_o && !aligned(o.stage_o, 4)) || (o.anc_out && !aligned(o.anc_out, 4)))
     return fail(XATTN_EINVAL, "tap arrays must be 4-byte aligned");
-  const size_t need = workspace_bytes_for(s, step);
+  const size_t need = pl.workspace_bytes;
   if (need > 0) {
     if (!workspace) return fail(XATTN_EINVAL, "this step needs a workspace (xattn_workspace_size)");
     if (workspace_bytes < need) return fail(XATTN_EINVAL, "workspace is smaller than xattn_workspace_size");
@@ -150,9 +225,10 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   p.unshared_v = unshared_v;
   p.parent_idx = parent_idx;
   p.out = out;
-  p.lse = lse;
-  p.stage_ml = stage_ml;
-  p.stage_o = stage_o;
+  p.lse = o.lse;
+  p.stage_ml = o.stage_ml;
+  p.stage_o = o.stage_o;
+  p.anc_out = o.anc_out;
   p.R = s->num_requests;
   p.BW = s->beam_width;
   p.Hq = s->num_q_heads;
@@ -165,43 +241,44 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   p.M = p.BW * p.G;
   p.scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)p.D);
   p.scale_log2 = p.scale * 1.4426950408889634f;
-  p.anc = nullptr;
-  p.tok_ml = nullptr;
-  p.tok_o = nullptr;
-  p.part_ml = nullptr;
-  p.part_o = nullptr;
+  // the debug taps report each stage's true maximum
+  p.lazy_log2 = o.taps ? 0.f : xattn::kLazyRescaleLog2;
   p.n_split = 1;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   // timing events: start bound to the call's first kernel, stop to its last
-  xattn::LaunchEvents ev_first{ev.start, nullptr}, ev_last{nullptr, ev.stop};
-  bool first = true;
-  auto first_ev = [&]() {
-    xattn::LaunchEvents r = first ? ev_first : xattn::LaunchEvents{};
-    first = false;
+  int launched = 0;
+  auto evs = [&]() {
+    xattn::LaunchEvents r{launched == 0 ? o.ev.start : nullptr,
+                          launched == pl.kernels - 1 ? o.ev.stop : nullptr};
+    ++launched;
     return r;
   };
-  if (need > 0) {
+  if (pl.ancestor_walk != kWalkInKernel) {
     int32_t *anc = static_cast<int32_t *>(workspace);
     const xattn::AncLayout lay{(int64_t)(step + 1) * p.BW, 1, p.BW};  // [R][step+1][BW]
-    if (seg_map_bytes_for(s, step) > 0) {
+    if (pl.ancestor_walk == kWalkSegmented) {
       int32_t *fmap = reinterpret_cast<int32_t *>(static_cast<uint8_t *>(workspace) +
                                                   anc_bytes_for(s, step));
       // both walk kernels go in the call's timing window
-      xattn::LaunchEvents ev_walk = first_ev();
+      xattn::LaunchEvents ev_walk{launched == 0 ? o.ev.start : nullptr, nullptr};
+      launched += 2;
       e = xattn::launch_resolve_ancestors_segmented(parent_idx, p.R, p.BW, p.S, step, anc, lay,
                                                     fmap, hs, ev_walk);
     } else {
-      e = xattn::launch_resolve_ancestors(parent_idx, p.R, p.BW, p.S, step, anc, lay, hs,
-                                          first_ev());
+      e = xattn::launch_resolve_ancestors(parent_idx, p.R, p.BW, p.S, step, anc, lay, hs, evs());
     }
     if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
     p.anc = anc;
+    if (o.anc_out) {
+      // the slots the walk kernels wrote, in the same layout
+      e = hipMemcpyAsync(o.anc_out, anc, (size_t)p.R * (step + 1) * p.BW * sizeof(int32_t),
+                         hipMemcpyDeviceToDevice, hs);
+      if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+    }
   }
-  const bool staged_bf16 =
-      s->dtype == XATTN_BF16 && !per_beam && (taps || p.M > xattn::kPerBeamMaxRows);
-  if (need > 0 && staged_bf16 && !taps) {
+  if (pl.unshared_kernel) {
     // deep chains: the Unshared stage runs first with one workgroup per
     // (request, beam, KV head), so the gather of every beam's token rows
     // spreads over the whole GPU; the staged kernel starts from its partials
@@ -211,27 +288,25 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
     w += round256(rows_of(s) * 2 * sizeof(float));
     p.tok_o = reinterpret_cast<float *>(w);
     w += round256(rows_of(s) * (size_t)s->head_dim * sizeof(float));
-    const int ns = key_splits_for(s, step);
-    if (ns > 1) {
-      p.n_split = ns;
+    if (pl.key_splits > 1) {
+      p.n_split = pl.key_splits;
       p.part_ml = reinterpret_cast<float *>(w);
-      w += round256((size_t)ns * rows_of(s) * 2 * sizeof(float));
+      w += round256((size_t)pl.key_splits * rows_of(s) * 2 * sizeof(float));
       p.part_o = reinterpret_cast<float *>(w);
     }
-    e = xattn::launch_token_partials_bf16(p, hs, first_ev());
+    e = xattn::launch_token_partials_bf16(p, hs, evs());
     if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
   }
-  // with key splits the merge kernel is the call's last
-  xattn::LaunchEvents ev_main = p.n_split > 1 ? first_ev() : (first ? ev : ev_last);
-  if (s->dtype == XATTN_F32)
+  const xattn::LaunchEvents ev_main = evs();
+  if (pl.kernel == XATTN_KERNEL_F32)
     e = xattn::launch_decode_f32(p, hs, ev_main);  // per query row already: also the per-beam form
-  else if (!staged_bf16)
+  else if (pl.kernel == XATTN_KERNEL_PER_BEAM_BF16)
     e = xattn::launch_decode_per_beam_bf16(p, hs, ev_main);
   else
-    e = xattn::launch_decode_bf16(p, taps, hs, ev_main);
+    e = xattn::launch_decode_bf16(p, o.taps, hs, ev_main);
   if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
-  if (p.n_split > 1) {
-    e = xattn::launch_merge_splits_bf16(p, hs, ev_last);
+  if (pl.key_splits > 1) {
+    e = xattn::launch_merge_splits_bf16(p, hs, evs());
     if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
   }
   g_last_error[0] = '\0';
@@ -454,7 +529,20 @@ xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *s
                           const int32_t *parent_idx, int32_t step, void *out, void *workspace,
                           size_t workspace_bytes, void *stream) {
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
-             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream);
+             out, workspace, workspace_bytes, stream, RunOpts{});
+}
+
+xattn_status xattn_decode_with_ancestors(const xattn_shape *shape, const void *q,
+                                         const void *shared_k, const void *shared_v,
+                                         const int32_t *prompt_len, const void *unshared_k,
+                                         const void *unshared_v, const int32_t *parent_idx,
+                                         int32_t step, void *out, int32_t *anc, void *workspace,
+                                         size_t workspace_bytes, void *stream) {
+  RunOpts o;
+  o.anc_out = anc;
+  o.want_anc = true;
+  return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+             out, workspace, workspace_bytes, stream, o);
 }
 
 xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const void *shared_k,
@@ -463,8 +551,13 @@ xattn_status xattn_decode_debug(const xattn_shape *shape, const void *q, const v
                                 const int32_t *parent_idx, int32_t step, void *out, float *lse,
                                 float *stage_ml, float *stage_o, void *workspace,
                                 size_t workspace_bytes, void *stream) {
+  RunOpts o;
+  o.lse = lse;
+  o.stage_ml = stage_ml;
+  o.stage_o = stage_o;
+  o.taps = true;
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
-             out, lse, stage_ml, stage_o, true, workspace, workspace_bytes, stream);
+             out, workspace, workspace_bytes, stream, o);
 }
 
 xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const void *shared_k,
@@ -474,11 +567,11 @@ xattn_status xattn_decode_timed(const xattn_shape *shape, const void *q, const v
                                 void *workspace, size_t workspace_bytes, void *stream,
                                 void *start_event, void *stop_event) {
   if (!start_event || !stop_event) return fail(XATTN_EINVAL, "both timing events are required");
-  xattn::LaunchEvents ev;
-  ev.start = static_cast<hipEvent_t>(start_event);
-  ev.stop = static_cast<hipEvent_t>(stop_event);
+  RunOpts o;
+  o.ev.start = static_cast<hipEvent_t>(start_event);
+  o.ev.stop = static_cast<hipEvent_t>(stop_event);
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
-             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream, ev);
+             out, workspace, workspace_bytes, stream, o);
 }
 
 xattn_status xattn_decode_per_beam(const xattn_shape *shape, const void *q, const void *shared_k,
@@ -486,8 +579,10 @@ xattn_status xattn_decode_per_beam(const xattn_shape *shape, const void *q, cons
                                    const void *unshared_k, const void *unshared_v,
                                    const int32_t *parent_idx, int32_t step, void *out,
                                    void *workspace, size_t workspace_bytes, void *stream) {
+  RunOpts o;
+  o.per_beam = true;
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
-             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream, {}, true);
+             out, workspace, workspace_bytes, stream, o);
 }
 
 xattn_status xattn_decode_per_beam_timed(const xattn_shape *shape, const void *q,
@@ -498,11 +593,19 @@ xattn_status xattn_decode_per_beam_timed(const xattn_shape *shape, const void *q
                                          size_t workspace_bytes, void *stream, void *start_event,
                                          void *stop_event) {
   if (!start_event || !stop_event) return fail(XATTN_EINVAL, "both timing events are required");
-  xattn::LaunchEvents ev;
-  ev.start = static_cast<hipEvent_t>(start_event);
-  ev.stop = static_cast<hipEvent_t>(stop_event);
+  RunOpts o;
+  o.per_beam = true;
+  o.ev.start = static_cast<hipEvent_t>(start_event);
+  o.ev.stop = static_cast<hipEvent_t>(stop_event);
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
-             out, nullptr, nullptr, nullptr, false, workspace, workspace_bytes, stream, ev, true);
+             out, workspace, workspace_bytes, stream, o);
+}
+
+xattn_status xattn_plan_decode(const xattn_shape *shape, int32_t step, xattn_plan *plan) {
+  if (!plan) return fail(XATTN_EINVAL, "plan is NULL");
+  const xattn_status st = make_plan(shape, step, false, false, plan);
+  if (st == XATTN_OK) g_last_error[0] = '\0';
+  return st;
 }
 
 size_t xattn_workspace_size(const xattn_shape *shape, int32_t step) {

@@ -48,6 +48,8 @@
 // writes each stage's (m, l, o) and merges them explicitly at the end.
 #include <hip/hip_ext.h>
 
+#include <algorithm>
+
 #include "xattn_internal.h"
 
 namespace xattn {
@@ -63,8 +65,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 constexpr int KT = 64;      // keys per shared-stage tile
 constexpr int NSTAGE = 4;   // LDS ring depth (tiles in flight = NSTAGE - 1)
 
-__device__ inline float lo_bf16(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ inline float hi_bf16(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -104,9 +104,9 @@ __device__ inline int xcd_logical_block(int b, int n) {
 }
 
 // A row's running maximum is only raised when a tile exceeds it by more
-// than 2^8 in the exp2 domain; until then p = exp2(s - m) may exceed 1 (by
-// at most 256), which fp32 sums and bf16 P hold without loss of range.
-constexpr float kLazyRescaleLog2 = 8.0f;
+// than p.lazy_log2 (kLazyRescaleLog2 = 8 on the decode path) in the exp2
+// domain; until then p = exp2(s - m) may exceed 1 (by at most 256), which
+// fp32 sums and bf16 P hold without loss of range.
 
 // s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8) waiting for vmcnt <= VM and lgkmcnt == 0.
@@ -591,99 +591,6 @@ __device__ __forceinline__ void pv_tile_max(const uint8_t *vt, const bf16x8 (&pf
   }
 }
 
-// Unshared stage for levels t_first, t_first + t_stride, ... <= step:
-// the beam's own generated token at each level (its ancestor slot), folded
-// into `st` by the same online-softmax update.  Each lane holds half of the
-// query and half of the output dims, so a score is a pair sum and its
-// weight is counted in l by lane half 0 only.
-// One generated token's K and V row, as the lanes of a row hold them: lane
-// half hl takes elements [8 hl, 8 hl + 8) of every 16 of K and the four
-// element groups of V the O^T accumulator layout gives it.
-template <int D>
-struct TokenRows {
-  uint4 kr[D / 16];
-  uint2 vr[D / 32][4];
-};
-
-template <int D>
-__device__ __forceinline__ void load_token(TokenRows<D> &tr, const uint16_t *ukg,
-                                           const uint16_t *uvg, int64_t roff, int hl) {
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    tr.kr[ks] = *reinterpret_cast<const uint4 *>(ukg + roff + ks * 16 + hl * 8);
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      tr.vr[db][j] = *reinterpret_cast<const uint2 *>(uvg + roff + db * 32 + 8 * j + 4 * hl);
-}
-
-// Online-softmax update of a row's state with one token (dot product on
-// the VALU, bf16 pairs into fp32; the pair of lanes holding the row adds
-// its two halves).
-template <int D>
-__device__ __forceinline__ void add_token(Rows<D> &st, const bf16x8 (&qf)[D / 16],
-                                          const TokenRows<D> &tr, float c, int hl) {
-  float part = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const uint4 kw = tr.kr[ks];
-    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16x2 qa = {qf[ks][2 * e], qf[ks][2 * e + 1]};
-      part = __builtin_amdgcn_fdot2_f32_bf16(qa, __builtin_bit_cast(bf16x2, kk[e]), part, false);
-    }
-  }
-  const float sc = pair_sum(part);
-  const float mn = fmaxf(st.m, sc);
-  const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // 0 while m is -inf
-  const float pr = __builtin_amdgcn_exp2f((sc - mn) * c);
-  st.l = st.l * alpha + (hl == 0 ? pr : 0.f);
-  st.m = mn;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint2 v = tr.vr[db][j];
-      st.O[db][4 * j + 0] = fmaf(st.O[db][4 * j + 0], alpha, pr * lo_bf16(v.x));
-      st.O[db][4 * j + 1] = fmaf(st.O[db][4 * j + 1], alpha, pr * hi_bf16(v.x));
-      st.O[db][4 * j + 2] = fmaf(st.O[db][4 * j + 2], alpha, pr * lo_bf16(v.y));
-      st.O[db][4 * j + 3] = fmaf(st.O[db][4 * j + 3], alpha, pr * hi_bf16(v.y));
-    }
-  }
-}
-
-// Unshared stage for the row this lane pair holds: the tokens at levels
-// t_first, t_first - t_stride, ... >= 0, each the row of the beam's
-// ancestor slot at that level.  Levels are walked downwards so that the
-// first one can be the current level, whose slot is the beam itself: its
-// rows may have been loaded before the ancestor walk (`pre`, when has_pre).
-template <int D>
-__device__ __forceinline__ void unshared_tokens(Rows<D> &st, const bf16x8 (&qf)[D / 16],
-                                                const uint16_t *ukg, const uint16_t *uvg,
-                                                const int32_t *anc_row, const int32_t *anc_ws,
-                                                int64_t anc_ws_base, int BW, int t_first,
-                                                int t_stride, float c, int lane,
-                                                const TokenRows<D> &pre, bool has_pre) {
-  const int hl = lane >> 5;
-  if (has_pre && t_first >= 0) {
-    add_token<D>(st, qf, pre, c, hl);
-    t_first -= t_stride;
-  }
-  TokenRows<D> tr;
-#pragma unroll 1
-  for (int t = t_first; t >= 0; t -= t_stride) {
-    const int slot =
-        anc_ws ? clampi(anc_ws[anc_ws_base + (int64_t)t * BW], 0, BW - 1) : anc_row[t];
-    load_token<D>(tr, ukg, uvg, ((int64_t)t * BW + slot) * D, hl);
-    add_token<D>(st, qf, tr, c, hl);
-  }
-}
-
-// Parent rows of levels 1..step are staged in LDS for the ancestor walk
-// when they fit this many ints; longer chains are resolved beforehand into
-// the workspace.
 // Generated-token rows of a row block, gathered into LDS in the layout of
 // the prompt tiles, in blocks of 32 rows.  Row group g of the block has
 // n_blk blocks; block b of it holds its tokens 32 b .. 32 b + 31, token i
@@ -849,10 +756,81 @@ __device__ __forceinline__ void token_block(Rows<D> &st, const bf16x8 (&qf)[D / 
   pv_tile<D, KSPLIT>(vb, pf, st, kh, fo);
 }
 
+// Online-softmax state of query row `ri` from the Unshared-stage partial
+// (m, l, unnormalised o) written by the token-partials kernel: l goes to lane
+// half 0 (a row's l is the sum over the lane pair).
+template <int D>
+__device__ __forceinline__ void seed_rows(Rows<D> &s, const DecodeParams &p, int64_t ri, int hl) {
+  s.m = p.tok_ml[ri * 2 + 0];
+  s.l = hl == 0 ? p.tok_ml[ri * 2 + 1] : 0.f;
+  const float *po = p.tok_o + ri * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = *reinterpret_cast<const float4 *>(po + db * 32 + 8 * j + 4 * hl);
+      s.O[db][4 * j + 0] = v.x;
+      s.O[db][4 * j + 1] = v.y;
+      s.O[db][4 * j + 2] = v.z;
+      s.O[db][4 * j + 3] = v.w;
+    }
+}
+
+// Key half 1 of a row group hands its state to key half 0 through LDS (xo:
+// O, 16 bytes per lane and step; xs: m, then l), and key half 0 folds it in.
+template <int D>
+__device__ __forceinline__ void half_put(const Rows<D> &s, float4 *xo, float *xs, int lane) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xo[(db * 4 + j) * 64 + lane] =
+          make_float4(s.O[db][4 * j], s.O[db][4 * j + 1], s.O[db][4 * j + 2], s.O[db][4 * j + 3]);
+  xs[lane] = s.m;
+  xs[64 + lane] = s.l;
+}
+
+template <int D>
+__device__ __forceinline__ void half_merge(Rows<D> &s, const float4 *xo, const float *xs, float c,
+                                           int lane) {
+  const float m2 = xs[lane];
+  const float l2 = xs[64 + lane];
+  float a1 = 1.f, a2 = 0.f;
+  if (m2 > s.m) {
+    a1 = __builtin_amdgcn_exp2f((s.m - m2) * c);  // 0 when m is -inf
+    a2 = 1.f;
+    s.m = m2;
+  } else if (m2 != -INFINITY) {
+    a2 = __builtin_amdgcn_exp2f((m2 - s.m) * c);
+  }
+  s.l = s.l * a1 + l2 * a2;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 o2 = xo[(db * 4 + j) * 64 + lane];
+      s.O[db][4 * j + 0] = s.O[db][4 * j + 0] * a1 + o2.x * a2;
+      s.O[db][4 * j + 1] = s.O[db][4 * j + 1] * a1 + o2.y * a2;
+      s.O[db][4 * j + 2] = s.O[db][4 * j + 2] * a1 + o2.z * a2;
+      s.O[db][4 * j + 3] = s.O[db][4 * j + 3] * a1 + o2.w * a2;
+    }
+}
+
+// Parent rows of levels 1..step are copied to LDS for the in-kernel walk
+// when they hold at most this many ints and the workgroup's LDS allows.
 constexpr int kParentLdsInts = 2048;
 
-__host__ __device__ inline bool stage_parents_in_lds(int step, int BW) {
-  return step > 0 && (int64_t)step * BW <= kParentLdsInts;
+// Static LDS of the kernel: the tile ring (K tiles of all stages, then V
+// tiles), then token block 0 (32 rows of K, then of V).
+template <int D>
+constexpr int kTilesLdsBytes = 2 * NSTAGE * TileGeom<D>::TILE_BYTES + 2 * 32 * TileGeom<D>::RB;
+
+// Most beams the query rows of one workgroup belong to: row blocks start at
+// multiples of `rows`, so when G divides `rows` a block holds rows / G whole
+// beams; otherwise it may also hold part of a beam at either end.
+int beams_per_block(int rows, int G, int BW) {
+  const int nb = rows % G == 0 ? rows / G : (rows - 1) / G + 2;
+  return std::min(nb, BW);
 }
 
 template <int D, int RG, int KSPLIT, bool TAPS>
@@ -872,8 +850,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // compiler see that a copy into one stage does not alias reads of
   // another (so it adds no wait of its own in front of those reads).
   // After the ring, token block 0 (32 rows of K, then of V).
-  __shared__ __attribute__((aligned(1024)))
-  uint8_t tiles[2 * NSTAGE * Gm::TILE_BYTES + 2 * 32 * Gm::RB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[kTilesLdsBytes<D>];
   // dynamic: ancestor slots [beams of the block][step + 1], then (when
   // staged) the parent rows [step][BW] of levels 1..step
   extern __shared__ int32_t dyn_lds[];
@@ -897,17 +874,18 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // wait does not involve the vector-memory counter the copies run on
   const int L = clampi(p.prompt_len[r], 0, p.Lmax);
   const float c = p.scale_log2;
-  // in raw dot-product units; the debug variant reports the stages' true
-  // maxima, so it raises m on every increase
-  const float thr = TAPS ? 0.f : kLazyRescaleLog2 / c;
+  // in raw dot-product units; the debug entry passes 0, so that the stages'
+  // maxima it reports are the true ones
+  const float thr = p.lazy_log2 / c;
 
   const int row0 = rb * ROWS;
+  // the beams rows row0 .. row0 + ROWS - 1 (clipped to the M rows) belong to
   const int b_lo = row0 / G;
-  const int nb = min(BW - b_lo, (ROWS - 1) / G + 2);
+  const int nb = (min(row0 + ROWS, p.M) - 1) / G - b_lo + 1;
   int32_t *anc_lds = dyn_lds;
   int32_t *par_lds = dyn_lds + nb * (step + 1);
   const bool walk_here = p.anc == nullptr;
-  const bool staged = walk_here && stage_parents_in_lds(step, BW);
+  const bool staged = walk_here && p.stage_par != 0;
 
   // ---- copies into LDS that depend on nothing, issued before the tile
   // copies (vmcnt counts in issue order, so the wait for tile 0 covers
@@ -1008,8 +986,9 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // into the stage that step frees, in the last two steps, where no prompt
   // tile remains to copy, so it lands while the last prompt tiles are
   // consumed; chunks that find no such step are copied after the loop.
-  // Deep chains (slots in the workspace) read their rows directly.
-  const bool lds_tokens = !TAPS && walk_here;
+  // Deep chains (slots in the workspace) get their Unshared stage from a
+  // kernel run beforehand (below).
+  const bool lds_tokens = walk_here;
   const int nlev = step + 1;
   const int nbr_max = (32 % G == 0) ? 32 / G : 32 / G + 2;  // beams 32 rows can touch
   const int n_blk = (nbr_max * nlev + 31) / 32;
@@ -1091,46 +1070,28 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     qf[ks] = *reinterpret_cast<const bf16x8 *>(qlds + ql * Gm::RB +
                                                 (((2 * ks + hl) ^ Gm::swz(ql)) << 4));
 
-  Rows<D> st;
+  // st: the online-softmax state of the row; with TAPS, of the Shared stage
+  // alone, and su that of the Unshared stage (the debug entry keeps the
+  // stages apart and merges them explicitly at the end)
+  Rows<D> st, su;
   st.clear();
-  const int32_t *anc_row = anc_lds + (beam - b_lo) * (step + 1);
-  const int64_t anc_ws_base = (int64_t)r * (step + 1) * BW + beam;
-  if constexpr (!TAPS) {
-    // deep chains: key half kh takes levels step - kh, step - kh - 2, ...;
-    // the state seeds the online softmax the prompt tiles continue
-    if (!walk_here) {
-      if (p.tok_o) {
-        // the Unshared stage was computed beforehand, one workgroup per
-        // (request, beam, KV head): key split 0 starts from its partial;
-        // key half 1 starts empty, and l lives in lane half 0 (the row
-        // total is the pair's sum)
-        if (kh == 0 && split == 0) {
-          const int64_t ro = qoff / D;
-          st.m = p.tok_ml[ro * 2 + 0];
-          st.l = hl == 0 ? p.tok_ml[ro * 2 + 1] : 0.f;
-          const float *po = p.tok_o + ro * D;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float4 v = *reinterpret_cast<const float4 *>(po + db * 32 + 8 * j + 4 * hl);
-              st.O[db][4 * j + 0] = v.x;
-              st.O[db][4 * j + 1] = v.y;
-              st.O[db][4 * j + 2] = v.z;
-              st.O[db][4 * j + 3] = v.w;
-            }
-        }
-        // the compiler counts these loads, not the tile copies issued before
-        // them: left pending, they would make it wait for vmcnt to reach 0 at
-        // their first use inside the tile loop, every iteration, draining the
-        // copy pipeline; completing them here clears that for the whole loop
-        wait_vm_lgkm0<0>();
-      } else {
-        TokenRows<D> none;
-        unshared_tokens<D>(st, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step - kh, KSPLIT,
-                           c, lane, none, false);
-      }
+  su.clear();
+  if (!walk_here) {
+    // deep chains: the Unshared stage was computed beforehand, one workgroup
+    // per (request, beam, KV head); key half 0 of key split 0 starts from its
+    // partial (key half 1 starts empty; l lives in lane half 0, the row
+    // total being the pair's sum)
+    if (kh == 0 && split == 0) {
+      if constexpr (TAPS)
+        seed_rows<D>(su, p, qoff / D, hl);
+      else
+        seed_rows<D>(st, p, qoff / D, hl);
     }
+    // the compiler counts these loads, not the tile copies issued before
+    // them: left pending, they would make it wait for vmcnt to reach 0 at
+    // their first use inside the tile loop, every iteration, draining the
+    // copy pipeline; completing them here clears that for the whole loop
+    wait_vm_lgkm0<0>();
   }
 
   // ---- Shared stage.  Per tile t (in stage t % NSTAGE) but the last: wait
@@ -1221,7 +1182,7 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   // block 0 and the chunks copied in the loop (chunk c in stage
   // (chunk_t0 + c + 3) % NSTAGE) first, then any other chunks one at a time
   // through stage 0.
-  if constexpr (!TAPS) {
+  {
     if (lds_tokens) {
       const int n_pref = min(n_chunks, max(0, n_tiles - 1 - chunk_t0));
       const int grow = row0 + rg * 32;
@@ -1256,8 +1217,12 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
           const int gb = b * RG + rg;
           if ((gb == 0) != (ch < 0) || (gb > 0 && ((gb - 1) >> 1) != ch)) continue;
           const int off = gb == 0 ? 0 : 32 * ((gb - 1) & 1) * Gm::RB;
-          token_block<D, KSPLIT>(st, qf, kt + off, vt + off, fo, kh, 32 * b, tok_lo, tok_hi, c,
-                                 thr, lane);
+          if constexpr (TAPS)
+            token_block<D, KSPLIT>(su, qf, kt + off, vt + off, fo, kh, 32 * b, tok_lo, tok_hi, c,
+                                   thr, lane);
+          else
+            token_block<D, KSPLIT>(st, qf, kt + off, vt + off, fo, kh, 32 * b, tok_lo, tok_hi, c,
+                                   thr, lane);
         }
       }
     }
@@ -1272,47 +1237,35 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     static_assert(NDB * 16 * 64 * 4 <= Gm::TILE_BYTES, "the exchanged O must fit a K tile");
     wait_vm_lgkm0<0>();
     lds_barrier();  // every wave is done with the tile stages
-    float4 *xo = reinterpret_cast<float4 *>(XATTN_KT(rg));   // O, 16 B per lane and step
-    float *xs = reinterpret_cast<float *>(XATTN_VT(rg));     // m, l
-    if (kh == 1) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          xo[(db * 4 + j) * 64 + lane] = make_float4(st.O[db][4 * j], st.O[db][4 * j + 1],
-                                                     st.O[db][4 * j + 2], st.O[db][4 * j + 3]);
-      xs[lane] = st.m;
-      xs[64 + lane] = st.l;
-    }
-    __syncthreads();
-    // the normalised rows of the plain path go out through LDS, stored by
-    // both key halves (below); other paths leave the writing to key half 0
-    if (kh == 1 && (TAPS || p.n_split > 1)) return;
-  }
-  if (KSPLIT == 2 && kh == 0) {
-    const float4 *xo = reinterpret_cast<const float4 *>(XATTN_KT(rg));
-    const float *xs = reinterpret_cast<const float *>(XATTN_VT(rg));
-    const float m2 = xs[lane];
-    const float l2 = xs[64 + lane];
-    float a1 = 1.f, a2 = 0.f;
-    if (m2 > st.m) {
-      a1 = __builtin_amdgcn_exp2f((st.m - m2) * c);  // 0 when m is -inf
-      a2 = 1.f;
-      st.m = m2;
-    } else if (m2 != -INFINITY) {
-      a2 = __builtin_amdgcn_exp2f((m2 - st.m) * c);
-    }
-    st.l = st.l * a1 + l2 * a2;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 o2 = xo[(db * 4 + j) * 64 + lane];
-        st.O[db][4 * j + 0] = st.O[db][4 * j + 0] * a1 + o2.x * a2;
-        st.O[db][4 * j + 1] = st.O[db][4 * j + 1] * a1 + o2.y * a2;
-        st.O[db][4 * j + 2] = st.O[db][4 * j + 2] * a1 + o2.z * a2;
-        st.O[db][4 * j + 3] = st.O[db][4 * j + 3] * a1 + o2.w * a2;
+    if (p.anc_out && walk_here && k == 0 && split == 0) {
+      // the ancestor slots this workgroup walked, for the beams whose first
+      // query row lies in its block: anc_out [R][step + 1][BW]
+      const int bf = (row0 + G - 1) / G;
+      const int n = (min(row0 + ROWS, p.M) + G - 1) / G - bf;
+      for (int i = tid; i < n * (step + 1); i += NT) {
+        const int bi = i / (step + 1), t = i - bi * (step + 1);
+        p.anc_out[((int64_t)r * (step + 1) + t) * BW + bf + bi] = anc_lds[(bf - b_lo + bi) * (step + 1) + t];
       }
+    }
+    float4 *xo = reinterpret_cast<float4 *>(XATTN_KT(rg));
+    float *xs = reinterpret_cast<float *>(XATTN_VT(rg));
+    if (kh == 1) half_put<D>(st, xo, xs, lane);
+    __syncthreads();
+    if constexpr (TAPS) {
+      // the Shared states, then the Unshared states, through the same buffers
+      if (kh == 0) half_merge<D>(st, xo, xs, c, lane);
+      __syncthreads();
+      if (kh == 1) half_put<D>(su, xo, xs, lane);
+      __syncthreads();
+      if (kh == 1) return;
+      half_merge<D>(su, xo, xs, c, lane);
+    } else {
+      // the normalised rows of the plain path go out through LDS, stored by
+      // both key halves (below); the key-split path leaves the writing to
+      // key half 0
+      if (kh == 1 && p.n_split > 1) return;
+      if (kh == 0) half_merge<D>(st, xo, xs, c, lane);
+    }
   }
 
   // ---- Merge / epilogue
@@ -1341,13 +1294,8 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
     }
   }
   if constexpr (TAPS) {
-    // Shared partial (m, l, O) on its own; then the Unshared partial on its
-    // own; then their explicit OnlineSoftmax merge.
-    Rows<D> su;
-    su.clear();
-    TokenRows<D> su_none;
-    unshared_tokens<D>(su, qf, ukg, uvg, anc_row, p.anc, anc_ws_base, BW, step, 1, c, lane,
-                       su_none, false);
+    // the Shared partial (m, l, O) and the Unshared partial, each on its
+    // own, then their explicit OnlineSoftmax merge
     const float ls = pair_sum(st.l), lu = pair_sum(su.l);
     const float ms = st.m, mu = su.m;
     const float inv_s = ls > 0.f ? 1.f / ls : 0.f;
@@ -1445,28 +1393,48 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   }
 }
 
+template <int D, int RG, int KSPLIT>
+Bf16Geometry geometry_cfg(const DecodeParams &p) {
+  constexpr int ROWS = RG * 32;
+  Bf16Geometry g{};
+  g.rows = ROWS;
+  g.threads = RG * KSPLIT * 64;
+  g.grid = (int64_t)p.R * p.Hkv * ((p.M + ROWS - 1) / ROWS) * p.n_split;
+  g.static_lds = kTilesLdsBytes<D>;
+  g.beams_per_block = beams_per_block(ROWS, p.G, p.BW);
+  g.dyn_lds = 0;
+  g.stage_par = false;
+  if (p.anc == nullptr) {
+    // ancestor slots [beams of the block][step + 1]
+    g.dyn_lds = g.beams_per_block * (p.step + 1) * (int)sizeof(int32_t);
+    // parent rows, copied 64 ints per wave instruction: whole rounds of 64
+    const int par_bytes = (p.step * p.BW + 63) / 64 * 64 * (int)sizeof(int32_t);
+    if (p.step > 0 && (int64_t)p.step * p.BW <= kParentLdsInts &&
+        g.static_lds + g.dyn_lds + par_bytes <= kLdsLimit) {
+      g.stage_par = true;
+      g.dyn_lds += par_bytes;
+    }
+  }
+  return g;
+}
+
 template <int D, int RG, int KSPLIT, bool TAPS>
 hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream, LaunchEvents ev) {
   constexpr int ROWS = RG * 32;
   DecodeParams p = p0;
   p.n_rb = (p.M + ROWS - 1) / ROWS;
   if (TAPS && p.n_split != 1) return hipErrorInvalidValue;
-  const int64_t grid = (int64_t)p.R * p.Hkv * p.n_rb * p.n_split;
-  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  size_t dyn = 0;
-  if (p.anc == nullptr) {
-    const int nb = min(p.BW, (ROWS - 1) / p.G + 2);
-    dyn = (size_t)nb * (p.step + 1) * sizeof(int32_t);
-    // parent rows are copied 64 ints per wave instruction: whole rounds of 64
-    if (stage_parents_in_lds(p.step, p.BW))
-      dyn += (size_t)((p.step * p.BW + 63) / 64 * 64) * sizeof(int32_t);
-  }
+  const Bf16Geometry g = geometry_cfg<D, RG, KSPLIT>(p);
+  if (g.grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (g.static_lds + g.dyn_lds > kLdsLimit) return hipErrorInvalidConfiguration;
+  p.stage_par = g.stage_par ? 1 : 0;
+  const uint32_t dyn = (uint32_t)g.dyn_lds;
   if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
-                          dim3(RG * KSPLIT * 64), (uint32_t)dyn, stream, ev.start, ev.stop, 0u, p);
+    hipExtLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)g.grid),
+                          dim3(g.threads), dyn, stream, ev.start, ev.stop, 0u, p);
   else
-    hipLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)grid),
-                       dim3(RG * KSPLIT * 64), dyn, stream, p);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)g.grid),
+                       dim3(g.threads), dyn, stream, p);
   return hipGetLastError();
 }
 
@@ -1544,6 +1512,18 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p) {
 }  // namespace
 
 int bf16_rows_per_block(const DecodeParams &p) { return rows_per_block(p.M); }
+
+Bf16Geometry bf16_geometry(const DecodeParams &p) {
+  const int rows = rows_per_block(p.M);
+  if (p.D == 64) {
+    if (rows == 32) return geometry_cfg<64, 1, 2>(p);
+    if (rows == 64) return geometry_cfg<64, 2, 2>(p);
+    return geometry_cfg<64, 4, 2>(p);
+  }
+  if (rows == 32) return geometry_cfg<128, 1, 2>(p);
+  if (rows == 64) return geometry_cfg<128, 2, 2>(p);
+  return geometry_cfg<128, 4, 2>(p);
+}
 
 hipError_t launch_merge_splits_bf16(const DecodeParams &p, hipStream_t stream, LaunchEvents ev) {
   const int64_t rows = (int64_t)p.R * p.BW * p.Hq;

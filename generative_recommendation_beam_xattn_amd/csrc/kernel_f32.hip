@@ -46,12 +46,24 @@ struct StageState {
   }
 };
 
+static_assert(kWaves * 64 == kF32Threads, "threads per workgroup");
+
+// Static LDS: the walked ancestor slots, and per stage and wave (m, l, o).
+template <int D>
+struct F32Lds {
+  int32_t anc_s[kMaxInKernelLevels];
+  float red_m[2][kWaves], red_l[2][kWaves];
+  float red_o[2][kWaves][D];
+};
+
 template <int D>
 __global__ __launch_bounds__(kWaves * 64) void decode_f32_kernel(DecodeParams p) {
   constexpr int DL = D / 64;
-  __shared__ int32_t anc_s[kMaxInKernelLevels];
-  __shared__ float red_m[2][kWaves], red_l[2][kWaves];
-  __shared__ float red_o[2][kWaves][D];
+  __shared__ F32Lds<D> lds;
+  int32_t *anc_s = lds.anc_s;
+  float (*red_m)[kWaves] = lds.red_m;
+  float (*red_l)[kWaves] = lds.red_l;
+  float (*red_o)[kWaves][D] = lds.red_o;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -74,6 +86,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_f32_kernel(DecodeParams p)
     }
   }
   __syncthreads();
+  // the slots walked, when asked for: anc_out [R][step + 1][BW], written by
+  // the beam's first query row
+  if (p.anc == nullptr && p.anc_out && h == 0)
+    for (int t = threadIdx.x; t <= step; t += kWaves * 64)
+      p.anc_out[((int64_t)r * (step + 1) + t) * BW + b] = anc_s[t];
 
   const float *qp = static_cast<const float *>(p.q) + row * D;
   float qv[DL];
@@ -179,6 +196,8 @@ void launch_f32_d(const DecodeParams &p, unsigned grid, hipStream_t stream, Laun
 }
 
 }  // namespace
+
+int f32_lds_bytes(int D) { return D == 64 ? (int)sizeof(F32Lds<64>) : (int)sizeof(F32Lds<128>); }
 
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev) {
   const int64_t grid = (int64_t)p.R * p.BW * p.Hq;

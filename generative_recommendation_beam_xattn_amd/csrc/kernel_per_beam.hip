@@ -55,21 +55,34 @@ __device__ __forceinline__ float group_sum(float s) {
 }
 
 // A lane group's running maximum only moves when a score exceeds it by
-// more than 2^8 in the exp2 domain; until then exp2(s - m) may exceed 1 (by
-// at most 256), which the fp32 sums hold without loss of range.
-constexpr float kLazyRescaleLog2 = 8.0f;
+// more than p.lazy_log2 (8 on the decode path: 2^8) in the exp2 domain;
+// until then exp2(s - m) may exceed 1 (by at most 256), which the fp32 sums
+// hold without loss of range.
 
 // TOKENS: the Unshared stage alone (keys = the beam's tokens at levels
 // 0..step), written as an online-softmax partial for the staged kernel to
 // start from, instead of normalised output.
+static_assert(kWaves * 64 == kPerBeamThreads, "threads per workgroup");
+
+// Static LDS: the beam's ancestor slots, and each lane group's per-row state.
+template <int D>
+struct PerBeamLds {
+  static constexpr int NSG = kWaves * (64 / (D / 8));   // lane groups
+  int32_t anc_s[kAncLds];
+  float red_o[NSG][kRowsPerPass][D];
+  float red_ml[NSG][kRowsPerPass][2];
+};
+
 template <int D, bool TOKENS>
 __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodeParams p) {
   constexpr int LPK = D / 8;        // lanes per key row
   constexpr int KPW = 64 / LPK;     // key rows per wave per load
   constexpr int NSG = kWaves * KPW; // lane groups in the workgroup
-  __shared__ int32_t anc_s[kAncLds];
-  __shared__ float red_o[NSG][kRowsPerPass][D];
-  __shared__ float red_ml[NSG][kRowsPerPass][2];
+  static_assert(NSG == PerBeamLds<D>::NSG, "lane groups");
+  __shared__ PerBeamLds<D> lds;
+  int32_t *anc_s = lds.anc_s;
+  float (*red_o)[kRowsPerPass][D] = lds.red_o;
+  float (*red_ml)[kRowsPerPass][2] = lds.red_ml;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane / LPK, part = lane % LPK;
@@ -82,7 +95,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
   const int r = blockIdx.x / (p.Hkv * p.BW);
   const int step = p.step, BW = p.BW, G = p.G;
   const float c = p.scale_log2;
-  const float thr = kLazyRescaleLog2 / c;   // in raw dot-product units
+  const float thr = p.lazy_log2 / c;   // in raw dot-product units
 
   // the beam's ancestor slot at every level: walked here for short chains,
   // resolved into the workspace beforehand for deep ones
@@ -97,6 +110,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
       }
     }
     __syncthreads();
+    // the slots walked, when asked for: anc_out [R][step + 1][BW]
+    if (!TOKENS && p.anc_out && k == 0)
+      for (int t = tid; t <= step; t += kWaves * 64)
+        p.anc_out[((int64_t)r * (step + 1) + t) * BW + b] = anc_s[t];
   }
   // resolved slots (deep chains) are staged in LDS too when they fit, so a
   // token row's address waits on an LDS read, not a global one
@@ -272,6 +289,10 @@ __global__ __launch_bounds__(kWaves * 64) void decode_per_beam_kernel(DecodePara
 }
 
 }  // namespace
+
+int per_beam_lds_bytes(int D) {
+  return D == 64 ? (int)sizeof(PerBeamLds<64>) : (int)sizeof(PerBeamLds<128>);
+}
 
 hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream,
                                        LaunchEvents ev) {

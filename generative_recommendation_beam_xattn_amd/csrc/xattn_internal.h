@@ -21,6 +21,9 @@ constexpr int kMaxInKernelLevels = 16;
 constexpr int kPerBeamMaxRows = 8;
 // Most key splits one staged workgroup's prompt tiles are spread over.
 constexpr int kMaxKeySplits = 4;
+// On the decode path a running maximum is raised only when a score exceeds
+// it by more than 2^8 in the exp2 domain (DecodeParams::lazy_log2).
+constexpr float kLazyRescaleLog2 = 8.0f;
 
 // Largest beam width the beam-selection kernel takes.
 constexpr int kMaxTopkBeams = 512;
@@ -53,13 +56,18 @@ struct DecodeParams {
   float *lse;          // optional taps (debug entry only)
   float *stage_ml;
   float *stage_o;
+  int32_t *anc_out;    // optional [R][step+1][BW]: the ancestor slots the
+                       // Unshared stage gathered, written by the walking kernel
   int32_t R, BW, Hq, Hkv, D, Lmax, S, step;
   int32_t G;           // Hq / Hkv, query heads per KV head
   int32_t M;           // BW * G query rows per (request, KV head)
   int32_t n_rb;        // row blocks per (request, KV head)
   int32_t n_split;     // key splits of the prompt per row block (1: none)
+  int32_t stage_par;   // bf16 in-kernel walk: 1 = parent rows copied to LDS first
   float scale;         // softmax scale
   float scale_log2;    // scale * log2(e): scores go through exp2
+  float lazy_log2;     // a running maximum moves only when a score exceeds it by
+                       // more than this (exp2 units); 0 keeps the exact maximum
 };
 
 // Ancestor output layouts: element (r, b, t) lives at
@@ -85,9 +93,6 @@ hipError_t launch_decode_bf16(const DecodeParams &p, bool taps, hipStream_t stre
 hipError_t launch_decode_f32(const DecodeParams &p, hipStream_t stream, LaunchEvents ev = {});
 hipError_t launch_decode_per_beam_bf16(const DecodeParams &p, hipStream_t stream,
                                        LaunchEvents ev = {});
-// Unshared stage alone for deep chains (p.anc resolved): per query row its
-// partial (m, l) into p.tok_ml and unnormalised o into p.tok_o, in the units
-// of the staged kernel's online softmax (raw scores, exp2 with scale_log2).
 // Matrix-core throughput probe (measurement only): blocks workgroups of
 // kPeakThreads threads, iters rounds of independent bf16 MFMAs per wave;
 // out receives one float per thread.
@@ -100,6 +105,9 @@ hipError_t launch_peak_mfma(int32_t iters, int32_t blocks, float *out, hipStream
 hipError_t launch_peak_read(const void *src, int64_t bytes, int32_t blocks, uint32_t *out,
                             hipStream_t stream, LaunchEvents ev);
 
+// Unshared stage alone for deep chains (p.anc resolved): per query row its
+// partial (m, l) into p.tok_ml and unnormalised o into p.tok_o, in the units
+// of the staged kernel's online softmax (raw scores, exp2 with scale_log2).
 hipError_t launch_token_partials_bf16(const DecodeParams &p, hipStream_t stream,
                                       LaunchEvents ev = {});
 
@@ -161,6 +169,26 @@ int beam_topk_sample_len(int32_t BW, int32_t V);
 
 // Number of query rows one bf16 workgroup owns for this shape.
 int bf16_rows_per_block(const DecodeParams &p);
+
+// Launch geometry of the bf16 staged kernel for p (p.anc, p.step, p.BW,
+// p.G, p.M, p.D, p.n_split set): what launch_decode_bf16 would enqueue.
+struct Bf16Geometry {
+  int rows;            // query rows per workgroup
+  int threads;         // per workgroup
+  int64_t grid;        // workgroups
+  int static_lds;      // bytes of static LDS
+  int dyn_lds;         // bytes of dynamic LDS
+  int beams_per_block; // most beams one workgroup's rows touch
+  bool stage_par;      // parent rows staged in LDS for the in-kernel walk
+};
+// LDS one workgroup may use (gfx950: 160 KiB per compute unit).
+constexpr int kLdsLimit = 160 * 1024;
+Bf16Geometry bf16_geometry(const DecodeParams &p);
+// Static LDS bytes per workgroup of the f32 and per-beam kernels.
+int f32_lds_bytes(int D);
+int per_beam_lds_bytes(int D);
+constexpr int kF32Threads = 256;
+constexpr int kPerBeamThreads = 256;
 // Key splits: combine p.n_split partials (p.part_ml, p.part_o) into p.out.
 hipError_t launch_merge_splits_bf16(const DecodeParams &p, hipStream_t stream,
                                     LaunchEvents ev = {});

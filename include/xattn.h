@@ -102,6 +102,28 @@ xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *s
                           const int32_t *parent_idx, int32_t step, void *out,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * xattn_decode that also reports the ancestor slots its Unshared stage
+ * gathered (xGR summary, section 2.1: a beam reaches its generated tokens
+ * through the parent indices, token by token, with no copies):
+ *   anc [R][step+1][BW] int32, written: anc[r][t][b] = the slot of beam b's
+ *       ancestor at level t, i.e. anc[r][step][b] = b and
+ *       anc[r][t-1][b] = parent_idx[r][t][anc[r][t][b]] for t = step..1.
+ * Every other argument, the result and the errors are xattn_decode's, and
+ * the call enqueues exactly xattn_decode's kernels (xattn_plan_decode): the
+ * slots come from the code that walks the chain on the decode path.  Chains
+ * of at most 16 levels are walked inside the attention kernel, which writes
+ * the slots it walked to `anc`; deeper chains are resolved by the walk
+ * kernels into the workspace, from which they are copied to `anc` on the
+ * same stream.  Returns XATTN_EINVAL if anc is NULL or not 4-byte aligned.
+ */
+xattn_status xattn_decode_with_ancestors(const xattn_shape *shape, const void *q,
+                                         const void *shared_k, const void *shared_v,
+                                         const int32_t *prompt_len, const void *unshared_k,
+                                         const void *unshared_v, const int32_t *parent_idx,
+                                         int32_t step, void *out, int32_t *anc, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace xattn_decode / xattn_decode_debug need for this
  * shape and step (0 if none).  Returns (size_t)-1 if the shape or step is
  * invalid.  Chains of more than 16 levels need it: the resolved ancestor
@@ -115,12 +137,15 @@ xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *s
 size_t xattn_workspace_size(const xattn_shape *shape, int32_t step);
 
 /*
- * The ancestor slots a beam reaches through the parent chain, as used by the
- * Unshared stage (xGR summary, section 2.1: generated tokens are kept per
- * token and reached without copies when beams branch).
+ * The ancestor slots a beam reaches through the parent chain (xGR summary,
+ * section 2.1: generated tokens are kept per token and reached without
+ * copies when beams branch), on their own:
  *   anc [R][BW][step+1] int32, written: anc[r][b][step] = b and
  *   anc[r][b][t-1] = parent_idx[r][t][anc[r][b][t]] for t = step..1.
- * Runs the same device code xattn_decode uses for deep chains.
+ * Runs the chunked walk kernel that xattn_decode uses for chains of more
+ * than 16 levels that fit one segment (xattn_plan.ancestor_walk == 1).
+ * xattn_decode_with_ancestors reports the slots of the decode path itself,
+ * whichever walk it takes.
  */
 xattn_status xattn_resolve_ancestors(const xattn_shape *shape, const int32_t *parent_idx,
                                      int32_t step, int32_t *anc, void *stream);
@@ -128,9 +153,15 @@ xattn_status xattn_resolve_ancestors(const xattn_shape *shape, const int32_t *pa
 /*
  * xattn_decode that also exposes the stages (xGR summary, section 2.1: the
  * Shared and Unshared stages each produce max/sum statistics, and the
- * Merging stage combines them).  In this variant the two stages are
- * computed separately and merged explicitly; out matches xattn_decode's to
- * within rounding.  Every tap is optional (NULL skips it):
+ * Merging stage combines them).  In this variant the two stages are kept
+ * apart and merged explicitly; out matches xattn_decode's to within
+ * rounding.  The stages run the decode path's own code: the Shared stage
+ * the same prompt-tile loop, and the Unshared stage the same gathered
+ * token blocks on the matrix cores (chains of at most 16 levels) or the
+ * same per-beam token kernel (deeper chains), folded into a state of its
+ * own instead of the shared one.  Running maxima here are exact (the
+ * decode path raises them lazily), and a deep chain's prompt is never
+ * split over workgroups.  Every tap is optional (NULL skips it):
  *   lse       [R][BW][Hq] float32     m + ln(sum), the merged log-normaliser
  *   stage_ml  [2][R][BW][Hq][2] f32   (m, l) per stage: stage 0 Shared,
  *                                     stage 1 Unshared; m = max scaled score,
@@ -228,35 +259,40 @@ xattn_status xattn_reorder_unshared_timed(const xattn_shape *shape, void *unshar
                                           void *start_event, void *stop_event);
 
 /*
- * Measurement helper, not part of attention: a matrix-core throughput probe.
- * Launches `blocks` workgroups of 256 threads, each wave running `iters`
- * rounds of four independent v_mfma_f32_32x32x16_bf16 chains on register
- * operands, and writes one float per thread to `out` (device, at least
- * blocks * 256 floats; caller-owned).  *flops (if not NULL) receives the
- * floating-point operations the launch performs.  With both events given
- * (hipEvent_t, created and recorded by the caller) they are bound to the
- * dispatch, as in xattn_decode_timed; give both or neither.  The rate it
- * measures is what this chip's matrix cores deliver under a full load, at
- * the clock such a load holds: the reference against which the attention
- * kernels' MFMA fractions can be read beside the published peak.
- * Returns XATTN_EINVAL for iters or blocks < 1, a NULL or misaligned out,
- * or a single event.
+ * Where each call's work goes: what xattn_decode enqueues for a shape and
+ * step, computed on the host alone (no device is touched; usable without a
+ * GPU).  xattn_decode follows exactly this plan.
  */
-xattn_status xattn_peak_mfma_bf16(int32_t iters, int32_t blocks, float *out, void *stream,
-                                  void *start_event, void *stop_event, double *flops);
+typedef enum {
+  XATTN_KERNEL_STAGED_BF16 = 0,  /* bf16: the staged MFMA kernel */
+  XATTN_KERNEL_F32 = 1,          /* float32: one workgroup per query row */
+  XATTN_KERNEL_PER_BEAM_BF16 = 2 /* bf16 with <= 8 query rows per request and KV head */
+} xattn_kernel;
 
-/*
- * Measurement helper, not part of attention: an HBM read probe.  `blocks`
- * workgroups of 256 threads read the `bytes` (a positive multiple of 16) of
- * `src` (device, 16-byte aligned) once, with 16-byte non-temporal loads, and
- * write one word per thread to `out` (device, at least blocks * 256 words).
- * Events as for xattn_peak_mfma_bf16.  Its rate is the read bandwidth this
- * chip's HBM delivers to a plain stream: the reference for the attention
- * kernels' HBM fractions beside the published 8 TB/s.  Returns XATTN_EINVAL
- * for bad sizes, NULL or misaligned buffers, or a single event.
- */
-xattn_status xattn_peak_read(const void *src, int64_t bytes, int32_t blocks, uint32_t *out,
-                             void *stream, void *start_event, void *stop_event);
+typedef struct {
+  int32_t kernel;            /* an xattn_kernel: the attention kernel */
+  int32_t kernels;           /* kernels one call enqueues, 1 to 5 */
+  int32_t ancestor_walk;     /* 0: inside the attention kernel (<= 16 levels);
+                                1: one chunked walk kernel; 2: the segmented walk
+                                (two kernels), both into the workspace */
+  int32_t unshared_kernel;   /* 1: a per-beam kernel computes the Unshared stage
+                                first (bf16 chains deeper than 16 levels) */
+  int32_t key_splits;        /* 1, or the workgroups each prompt is split over,
+                                whose partials a last kernel merges */
+  int32_t rows_per_block;    /* query rows per attention workgroup */
+  int32_t threads_per_block; /* attention kernel */
+  int32_t lds_bytes;         /* attention kernel: LDS per workgroup, static + dynamic */
+  int32_t parents_in_lds;    /* in-kernel walk: parent rows copied to LDS first */
+  int32_t beams_per_block;   /* staged kernel, in-kernel walk: most beams one
+                                workgroup's query rows belong to */
+  int64_t grid;              /* attention kernel workgroups */
+  size_t workspace_bytes;    /* xattn_workspace_size(shape, step) */
+} xattn_plan;
+
+/* Fills *plan for xattn_decode(shape, ..., step, ...).  Returns the status
+ * xattn_decode would return for the shape and step (XATTN_EINVAL for a bad
+ * shape, step or NULL plan; XATTN_EUNSUPPORTED where no kernel fits). */
+xattn_status xattn_plan_decode(const xattn_shape *shape, int32_t step, xattn_plan *plan);
 
 /* Static description of a status code. */
 const char *xattn_status_string(xattn_status status);

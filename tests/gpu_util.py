@@ -54,3 +54,18 @@ def sample_rows(w, n, seed):
     corners = np.array([[0, 0, 0], [w.R - 1, w.BW - 1, w.Hq - 1], [0, w.BW - 1, 0],
                         [w.R - 1, 0, w.Hq - 1]], np.int32)
     return np.concatenate([corners, rows])
+
+
+_CACHE: dict = {}
+
+
+def workload(config, G=None):
+    """W.make(config, G), kept for the session (the full-size draws take
+    seconds); callers that change arrays copy them first."""
+    from generative_recommendation_beam_xattn_amd import workloads as W
+    key = (config, G)
+    if key not in _CACHE:
+        if len(_CACHE) >= 2:
+            _CACHE.pop(next(iter(_CACHE)))
+        _CACHE[key] = W.make(config, G)
+    return _CACHE[key]

@@ -38,12 +38,12 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_headers_found():
-    assert [os.path.basename(h) for h in HEADERS] == ["xattn.h", "xbeam.h"]
+    assert [os.path.basename(h) for h in HEADERS] == ["xattn.h", "xattn_measure.h", "xbeam.h"]
     assert len(declared_functions()) == len(B.EXPORTS)
 
 
 @pytest.mark.parametrize("lang", ["c", "c++"])
-@pytest.mark.parametrize("header", ["xattn.h", "xbeam.h"])
+@pytest.mark.parametrize("header", ["xattn.h", "xattn_measure.h", "xbeam.h"])
 def test_header_is_plain_c_and_cxx(lang, header, tmp_path):
     src = tmp_path / ("t." + ("c" if lang == "c" else "cpp"))
     src.write_text('#include "%s"\nint main(void){xattn_shape s; (void)s; return 0;}\n' % header)
@@ -123,6 +123,10 @@ def test_bad_shapes_rejected_before_launch(lib, kw, status, msg):
     assert msg in lib.xattn_last_error().decode()
     st = lib.xattn_resolve_ancestors(ctypes.byref(s), None, 0, None, None)
     assert st == status
+    st = lib.xattn_decode_with_ancestors(ctypes.byref(s), *([None] * 7), 0, None, None, None, 0,
+                                         None)
+    assert st == status
+    assert lib.xattn_plan_decode(ctypes.byref(s), 0, ctypes.byref(B.Plan())) == status
 
 
 def test_bad_step_and_null_pointers_rejected(lib):

@@ -3,9 +3,12 @@
 Bars: max abs error <= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs
 (fp32 accumulation, bf16 output); ancestor slots bit-exact.  Small shapes
 span several 64-key tiles, ragged tails of keys and query rows, every tiling
-the launcher picks, deep parent chains and the degenerate cases; the full
-workload sizes are checked on sampled rows the oracle computes one by one,
-in the launch configuration the benchmark times.
+the launcher picks, deep parent chains and the degenerate cases.  The full
+workload sizes are checked on every output row, in the launch configuration
+the benchmark times, with the ancestor slots the decode path itself walked;
+variants of them make the Unshared stage carry the result (empty prompts,
+and generated-token values scaled up), so that a wrong or missing ancestor
+row cannot hide under the 2e-2 bar.
 """
 import zlib
 
@@ -16,7 +19,7 @@ import torch
 import oracle
 import generative_recommendation_beam_xattn_amd as X
 from generative_recommendation_beam_xattn_amd import workloads as W
-from tests.gpu_util import TOL, DeviceWorkload, host_args, sample_rows, to_dev, to_f64
+from tests.gpu_util import TOL, DeviceWorkload, host_args, sample_rows, to_dev, to_f64, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +70,9 @@ SMALL = {
     # kernel (8 query rows per request and KV head)
     "rows8_per_beam_path": dict(R=3, BW=2, Hq=8, Hkv=2, D=128, L=[70, 0, 333], steps=[0, 2], S=3),
     "rows9_staged_path": dict(R=3, BW=3, Hq=6, Hkv=2, D=128, L=[70, 0, 333], steps=[0, 2], S=3),
+    # one head per KV head, 136 beams, 16 levels with the parent rows staged:
+    # 128 beams per workgroup fill the 160 KiB of LDS exactly
+    "lds_budget_g1_bw136": dict(R=2, BW=136, Hq=2, Hkv=2, D=128, L=[300, 700], steps=[15], S=16),
 }
 
 
@@ -83,39 +89,99 @@ def test_tiny_workload_all_steps():
     check_full(w, "tiny")
 
 
-@pytest.mark.parametrize("config", [2, 3, 4])
-def test_full_size_sampled(config):
-    w = W.make(config)
-    dw = DeviceWorkload(w)
-    for i, s in enumerate(w.steps):
-        say("[config %d] decode step %d sampled" % (config, s))
-        out = X.decode(*dw.args(i))
-        torch.cuda.synchronize()
-        rows = sample_rows(w, 512, seed=100 + s)
-        ref, _ = oracle.attend(*host_args(w, i), rows=rows)
-        got = to_f64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
-        err = np.max(np.abs(got - ref))
-        assert err <= TOL["bf16"], "config %d step %d: %g" % (config, s, err)
-        assert torch.isfinite(out.float()).all()
+def check_every_row(w, i, name, dw=None):
+    """Every output row of step index i, and the ancestor slots of the same
+    call, against the oracle; the slots' entry gives out bit for bit."""
+    dw = dw or DeviceWorkload(w)
+    s = w.steps[i]
+    say("[%s] decode step %d, every row (R=%d BW=%d Hq=%d Hkv=%d D=%d S=%d)" % (
+        name, s, w.R, w.BW, w.Hq, w.Hkv, w.D, w.S))
+    out = X.decode(*dw.args(i))
+    out2, anc = X.decode_with_ancestors(*dw.args(i))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    want = oracle.ancestors(w.parent_idx, s).transpose(0, 2, 1)
+    assert np.array_equal(anc.cpu().numpy(), want), "%s step %d: ancestor slots" % (name, s)
+    ref, _ = oracle.attend(*host_args(w, i))
+    err = np.max(np.abs(to_f64(out) - ref))
+    say("[%s] step %d: max abs err %.3g" % (name, s, err))
+    assert err <= TOL[w.dtype], "%s step %d: max abs err %g" % (name, s, err)
+    assert torch.isfinite(out.float()).all()
+
+
+# the serving workload at every step; the large-batch (skewed parents) and
+# wide-beam workloads at their last step
+FULL = [(2, 0), (2, 1), (2, 2), (3, 2), (4, 3)]
+
+
+@pytest.mark.parametrize("config,i", FULL)
+def test_full_size_every_row(config, i):
+    check_every_row(workload(config), i, "config %d" % config)
 
 
 @pytest.mark.parametrize("G", W.PREFIX_GROUPS)
-def test_prefix_sweep_sampled(G):
-    w = W.make(5, G)
+def test_prefix_sweep_every_row(G):
+    check_every_row(workload(5, G), 0, "prefix sweep G=%d" % G)
+
+
+# generated-token values scaled up where the prompt is not empty (the scale
+# ~ L / 16 keeps |out| below 4), and a quarter of the requests with no
+# prompt at all (out is then the Unshared stage alone)
+UNSHARED_SCALE = {2: 32, 3: 128, 4: 256}
+
+
+@pytest.mark.parametrize("config", [2, 3, 4])
+def test_unshared_stage_carries_the_result_every_row(config):
+    """Full-size shapes where the Unshared stage carries the result: a wrong,
+    missing or misplaced ancestor row moves its rows by >= 0.08 (measured
+    on the oracle by changing one parent), four times the bar."""
+    base = workload(config)
+    w = W.Workload(**{k: getattr(base, k) for k in base.__dataclass_fields__})
+    w.prompt_len = base.prompt_len.copy()
+    w.prompt_len[::4] = 0
+    v = W.bf16_bits_to_f32(base.unshared_v)
+    gamma = np.where(w.prompt_len > 0, np.float32(UNSHARED_SCALE[config]), np.float32(1.0))
+    w.unshared_v = W.to_bf16_bits(v * gamma[:, None, None, None, None])
+    check_every_row(w, len(w.steps) - 1, "config %d, Unshared-dominant" % config)
+
+
+@pytest.mark.parametrize("config", [1, 2, 3, 4])
+def test_ancestors_from_the_decode_path(config):
+    """The slots each step's own chain walk used (inside the attention
+    kernel for these short chains), against the oracle's, every step."""
+    w = W.make(config, R=min(W.CONFIGS[config]["R"], 8)) if config != 1 else W.make(1)
     dw = DeviceWorkload(w)
-    say("[prefix sweep G=%d] decode step %d sampled" % (G, w.steps[0]))
-    out = X.decode(*dw.args(0))
-    torch.cuda.synchronize()
-    rows = sample_rows(w, 256, seed=G)
-    ref, _ = oracle.attend(*host_args(w, 0), rows=rows)
-    got = to_f64(out)[rows[:, 0], rows[:, 1], rows[:, 2]]
-    assert np.max(np.abs(got - ref)) <= TOL["bf16"]
-    assert torch.isfinite(out.float()).all()
+    for i, s in enumerate(w.steps):
+        say("[config %d] decode_with_ancestors step %d" % (config, s))
+        _, anc = X.decode_with_ancestors(*dw.args(i))
+        torch.cuda.synchronize()
+        assert np.array_equal(anc.cpu().numpy(),
+                              oracle.ancestors(w.parent_idx, s).transpose(0, 2, 1))
+
+
+@pytest.mark.parametrize("BW,G,S,step", [(40, 4, 40, 39), (300, 1, 101, 100), (6, 2, 40, 39),
+                                         (2, 4, 30, 29), (3, 4, 20, 17)])
+def test_deep_chain_ancestors_from_the_decode_path(BW, G, S, step):
+    """Deep chains: the chunked walk (one segment) and the segmented walk
+    (300 beams: segments of 27 levels), on the staged, per-beam (2 beams x 4
+    heads) and f32 kernels, as xattn_decode runs them."""
+    for dtype in ("bf16", "f32"):
+        w = W.custom(name="deep", seed=BW + S, R=2, BW=BW, Hq=2 * G, Hkv=2, D=64, L=[70, 5],
+                     steps=[step], S=S, dtype=dtype)
+        dw = DeviceWorkload(w)
+        say("[deep ancestors BW=%d G=%d step=%d %s]" % (BW, G, step, dtype))
+        out, anc = X.decode_with_ancestors(*dw.args(0))
+        torch.cuda.synchronize()
+        assert np.array_equal(anc.cpu().numpy(),
+                              oracle.ancestors(w.parent_idx, step).transpose(0, 2, 1))
+        ref, _ = oracle.attend(*host_args(w, 0))
+        assert np.max(np.abs(to_f64(out) - ref)) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("config", [1, 2, 3, 4])
 def test_ancestors_exact(config):
-    w = W.make(config)
+    """xattn_resolve_ancestors, the chunked walk kernel on its own."""
+    w = W.make(config, R=min(W.CONFIGS[config]["R"], 8)) if config != 1 else W.make(1)
     par = to_dev(w.parent_idx)
     for s in w.steps:
         say("[config %d] resolve_ancestors step %d" % (config, s))
@@ -138,6 +204,11 @@ DEBUG = {
     "bf16_ragged": dict(R=3, BW=5, Hq=8, Hkv=2, D=128, L=[0, 77, 200], steps=[2]),
     "bf16_rowblocks": dict(R=2, BW=40, Hq=8, Hkv=2, D=64, L=[129, 64], steps=[1]),
     "bf16_deep": dict(R=2, BW=6, Hq=4, Hkv=2, D=128, L=[50, 0], steps=[39], S=40),
+    # the serving shape's tiling: prompts of more than three tiles (ancestor
+    # walk under tile 0, token chunks copied inside the tile loop) and an
+    # empty prompt, 128 beams, 4 query heads per KV head
+    "bf16_serving_tiling": dict(R=3, BW=128, Hq=16, Hkv=4, D=128, L=[700, 0, 257], steps=[2]),
+    "bf16_segmented_deep": dict(R=1, BW=40, Hq=4, Hkv=2, D=128, L=[100], steps=[150], S=151),
     "f32_ragged": dict(R=2, BW=5, Hq=8, Hkv=2, D=128, L=[0, 130], steps=[2], dtype="f32"),
 }
 
@@ -248,7 +319,7 @@ def test_per_beam_small_shapes(name, dtype):
 
 
 def test_per_beam_gr_serving_sampled_and_close_to_staged():
-    w = W.make(2)
+    w = workload(2)
     dw = DeviceWorkload(w)
     for i, s in enumerate(w.steps):
         say("[per-beam gr_serving] step %d" % s)
