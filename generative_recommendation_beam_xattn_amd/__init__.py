@@ -7,7 +7,7 @@ if it is missing: there is no fallback implementation.
 """
 from . import workloads  # noqa: F401  (seeded inputs; no attention arithmetic)
 
-_BINDING = ("decode", "decode_with_ancestors", "decode_per_beam", "decode_debug",
+_BINDING = ("decode", "decode_noalloc", "decode_with_ancestors", "decode_per_beam", "decode_debug",
             "resolve_ancestors", "workspace_size", "plan", "make_shape", "Shape",
             "beam_topk", "reorder_unshared", "trie_build", "ValidPaths", "library_path",
             "XattnError", "PreparedDecode", "load")

@@ -66,7 +66,8 @@ class Shape(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
-EXPORTS = ("xattn_decode", "xattn_decode_with_ancestors", "xattn_plan_decode",
+EXPORTS = ("xattn_decode", "xattn_decode_noalloc", "xattn_decode_with_ancestors",
+           "xattn_plan_decode",
            "xattn_decode_debug", "xattn_decode_timed", "xattn_decode_per_beam",
            "xattn_decode_per_beam_timed", "xattn_workspace_size",
            "xattn_resolve_ancestors", "xattn_reorder_unshared", "xattn_reorder_unshared_timed",
@@ -94,6 +95,8 @@ def load():
         i32, sz = ctypes.c_int32, ctypes.c_size_t
         lib.xattn_decode.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, sz, P]
         lib.xattn_decode.restype = ctypes.c_int
+        lib.xattn_decode_noalloc.argtypes = [S, P, P, P, P, P, P, P, i32, P, P]
+        lib.xattn_decode_noalloc.restype = ctypes.c_int
         lib.xattn_decode_with_ancestors.argtypes = [S, P, P, P, P, P, P, P, i32, P, P, P, sz, P]
         lib.xattn_decode_with_ancestors.restype = ctypes.c_int
         lib.xattn_plan_decode.argtypes = [S, i32, ctypes.POINTER(Plan)]
@@ -241,6 +244,25 @@ def decode(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx
                             _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v),
                             _ptr(parent_idx), int(step), _ptr(out), _ptr(ws), ws_bytes,
                             _stream(stream, q.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # XATTN_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+                   out, scale: float = 0.0, stream=None):
+    """xattn_decode_noalloc: decode into the caller's ``out`` with no
+    workspace; the library allocates nothing (deep chains use its scratch)."""
+    lib = load()
+    _validate(q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx)
+    if out is None or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must be given, with q's shape and dtype")
+    shape = make_shape(q, shared_k, unshared_k, scale)
+    _check(lib.xattn_decode_noalloc(ctypes.byref(shape), _ptr(q), _ptr(shared_k), _ptr(shared_v),
+                                    _ptr(prompt_len), _ptr(unshared_k), _ptr(unshared_v),
+                                    _ptr(parent_idx), int(step), _ptr(out),
+                                    _stream(stream, q.device)))
     return out
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/xattn.h"
 #include "../../include/xattn_measure.h"
@@ -313,6 +314,37 @@ xattn_status run(const xattn_shape *s, const void *q, const void *shared_k, cons
   return XATTN_OK;
 }
 
+// ---- device scratch of xattn_decode_noalloc: one file-scope array, which
+// each GPU the library runs on holds (its own copy, at its own address)
+// until the process ends.  Host code never uses the array's name as an
+// address: it takes each device's address once, with that device current,
+// and passes that.
+constexpr size_t kScratchBytes = size_t(XATTN_NOALLOC_SCRATCH_BYTES);
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the scratch array (looked up on its first
+// use on that device).
+xattn_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(XATTN_EUNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail(XATTN_EHIP, hipGetErrorString(e));
+    if (!p || !aligned(p, 256)) return fail(XATTN_EHIP, "scratch address is not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return XATTN_OK;
+}
+
 xattn_status beam_topk(const float *cum, const float *logp, const int32_t *token, int32_t R,
                        int32_t BW, int32_t V, float *new_score, int32_t *new_parent,
                        int32_t *new_token, int64_t out_stride, void *stream,
@@ -530,6 +562,32 @@ xattn_status xattn_decode(const xattn_shape *shape, const void *q, const void *s
                           size_t workspace_bytes, void *stream) {
   return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
              out, workspace, workspace_bytes, stream, RunOpts{});
+}
+
+xattn_status xattn_decode_noalloc(const xattn_shape *shape, const void *q, const void *shared_k,
+                                  const void *shared_v, const int32_t *prompt_len,
+                                  const void *unshared_k, const void *unshared_v,
+                                  const int32_t *parent_idx, int32_t step, void *out,
+                                  void *stream) {
+  xattn_plan pl;
+  xattn_status st = make_plan(shape, step, false, false, &pl);
+  if (st != XATTN_OK) return st;
+  if (pl.workspace_bytes == 0)
+    return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+               out, nullptr, 0, stream, RunOpts{});
+  if (pl.workspace_bytes > kScratchBytes) {
+    char msg[160];
+    snprintf(msg, sizeof msg,
+             "this step needs %zu bytes of workspace, more than the %zu-byte scratch of "
+             "xattn_decode_noalloc; use xattn_decode with a workspace",
+             pl.workspace_bytes, kScratchBytes);
+    return fail(XATTN_EINVAL, msg);
+  }
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != XATTN_OK) return st;
+  return run(shape, q, shared_k, shared_v, prompt_len, unshared_k, unshared_v, parent_idx, step,
+             out, ws, kScratchBytes, stream, RunOpts{});
 }
 
 xattn_status xattn_decode_with_ancestors(const xattn_shape *shape, const void *q,

@@ -124,6 +124,33 @@ xattn_status xattn_decode_with_ancestors(const xattn_shape *shape, const void *q
                                          int32_t step, void *out, int32_t *anc, void *workspace,
                                          size_t workspace_bytes, void *stream);
 
+/*
+ * xattn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument.  Arguments, result and errors are otherwise
+ * xattn_decode's, and the kernels are the same.  A step that needs a
+ * workspace (chains of more than 16 levels) uses a scratch array of
+ * XATTN_NOALLOC_SCRATCH_BYTES inside the library instead: one per GPU,
+ * which that GPU holds from the library's first use on it until the process
+ * ends.  The call allocates nothing.
+ *   - A shape and step whose xattn_workspace_size exceeds
+ *     XATTN_NOALLOC_SCRATCH_BYTES is rejected with XATTN_EINVAL before
+ *     anything is enqueued.
+ *   - The scratch is the current device's (hipGetDevice): `stream` must
+ *     belong to it.
+ *   - Every call on a GPU shares that GPU's scratch, and each call leaves
+ *     its contents behind; no call needs them cleared (every byte a call
+ *     reads it wrote first).  Calls that may overlap on one GPU -- on
+ *     different streams, or from different threads -- race on it: order
+ *     them on one stream, or use xattn_decode with a workspace per stream.
+ */
+#define XATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+xattn_status xattn_decode_noalloc(const xattn_shape *shape, const void *q, const void *shared_k,
+                                  const void *shared_v, const int32_t *prompt_len,
+                                  const void *unshared_k, const void *unshared_v,
+                                  const int32_t *parent_idx, int32_t step, void *out,
+                                  void *stream);
+
 /* Bytes of device workspace xattn_decode / xattn_decode_debug need for this
  * shape and step (0 if none).  Returns (size_t)-1 if the shape or step is
  * invalid.  Chains of more than 16 levels need it: the resolved ancestor
