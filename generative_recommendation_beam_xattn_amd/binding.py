@@ -55,7 +55,7 @@ class Plan(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
-KERNEL_STAGED_BF16, KERNEL_F32, KERNEL_PER_BEAM_BF16 = 0, 1, 2
+KERNEL_STAGED_BF16, KERNEL_F32, KERNEL_PER_BEAM_BF16, KERNEL_STAGED_BF16_PAIRED = 0, 1, 2, 3
 
 
 class Shape(ctypes.Structure):

@@ -155,6 +155,7 @@ xattn_status make_plan(const xattn_shape *s, int32_t step, bool per_beam, bool t
     static const int32_t resolved = 0;   // any non-null: slots come from the workspace
     p.anc = deep ? &resolved : nullptr;
     const xattn::Bf16Geometry g = xattn::bf16_geometry(p);
+    if (g.paired) pl->kernel = XATTN_KERNEL_STAGED_BF16_PAIRED;
     pl->rows_per_block = g.rows;
     pl->threads_per_block = g.threads;
     pl->grid = g.grid;

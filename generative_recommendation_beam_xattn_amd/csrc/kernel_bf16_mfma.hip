@@ -209,13 +209,13 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Geometry of the LDS tiles: per stage a K tile and a V tile (separate
-// LDS objects), each KT rows of D bf16, row-major, with the 16-byte slots
-// of row r permuted by swz(r).
-template <int D>
+// LDS objects), each KTILE rows of D bf16, row-major, with the 16-byte
+// slots of row r permuted by swz(r).
+template <int D, int KTILE = KT>
 struct TileGeom {
   static constexpr int RB = D * 2;                 // bytes per row
   static constexpr int SLOTS = D / 8;              // 16-byte slots per row
-  static constexpr int TILE_BYTES = KT * RB;       // one K (or V) tile
+  static constexpr int TILE_BYTES = KTILE * RB;    // one K (or V) tile
   static constexpr int ROWS_PER_COPY = 1024 / RB;  // rows one wave-wide 16-byte copy fills
   static constexpr int COPIES = 2 * TILE_BYTES / 1024;  // wave-wide copies per stage (K and V)
   // Slot permutation.  D = 128 (16 slots): swap the two 2-bit fields of
@@ -235,17 +235,17 @@ struct TileGeom {
 
 // Distance from a ring stage's K tile to its V tile (the V tiles of all
 // stages follow the K tiles of all stages).
-template <int D>
-__host__ __device__ constexpr int kVRegionOffset() { return NSTAGE * TileGeom<D>::TILE_BYTES; }
+template <int D, int KTILE = KT, int NST = NSTAGE>
+__host__ __device__ constexpr int kVRegionOffset() { return NST * TileGeom<D, KTILE>::TILE_BYTES; }
 
 // This wave's share of the COPIES wave-wide copies that fill one stage:
 // copy i moves 1 KiB = ROWS_PER_COPY rows of the K tile (first NQ copies)
 // or of the V tile.  Lane `lane` fetches row q * ROWS_PER_COPY + lane /
 // SLOTS, 16-byte chunk (lane % SLOTS) ^ swz(row), which lands in LDS slot
 // lane % SLOTS of that row.
-template <int D, int WAVES>
+template <int D, int WAVES, int KTILE = KT>
 struct CopyPlan {
-  using Gm = TileGeom<D>;
+  using Gm = TileGeom<D, KTILE>;
   static constexpr int NQ = Gm::TILE_BYTES / 1024;   // copies per K (or V) tile
   static constexpr int PER = Gm::COPIES / WAVES;
   static_assert(Gm::COPIES % WAVES == 0, "copies must split evenly over the waves");
@@ -267,12 +267,12 @@ struct CopyPlan {
 // shifted back to end at L), so only a prompt shorter than one tile needs
 // its rows clamped to the last one; clamped rows are always in bounds and
 // their scores are masked.
-template <int D, int WAVES, bool CLAMP, bool NT = true>
+template <int D, int WAVES, bool CLAMP, bool NT = true, int KTILE = KT>
 __device__ __forceinline__ void tile_copy(uint8_t *ktile, uint8_t *vtile,
-                                          const CopyPlan<D, WAVES> &cp, const uint16_t *skg,
+                                          const CopyPlan<D, WAVES, KTILE> &cp, const uint16_t *skg,
                                           const uint16_t *svg, int key0, int L, int wave) {
-  using Gm = TileGeom<D>;
-  using C = CopyPlan<D, WAVES>;
+  using Gm = TileGeom<D, KTILE>;
+  using C = CopyPlan<D, WAVES, KTILE>;
 #pragma unroll
   for (int i = 0; i < C::PER; ++i) {
     const int qi = wave * C::PER + i;
@@ -314,7 +314,7 @@ struct Rows {
 // db the row is 32*(ps/2) + 16*(ps%2) + 8*e2 + 4h + j/4 and the slot
 // (4db + 2g + (j/2)%2) ^ swz(row); swz(row) depends only on the lane and e2
 // (the ps terms are multiples of 16 rows), so ps is an immediate as well.
-template <int D>
+template <int D, int VREG = kVRegionOffset<D>()>
 struct FragOffsets {
   using Gm = TileGeom<D>;
   uint32_t k[D / 16];        // per ks
@@ -330,7 +330,7 @@ struct FragOffsets {
     // tiles to the V tiles of the ring, so that a V fragment's address is
     // (ring stage base + this register + an immediate below 64 KiB): the
     // V tiles themselves lie past the 16-bit offset field
-    const int kv_region = kVRegionOffset<D>();
+    const int kv_region = VREG;
 #pragma unroll
     for (int e2 = 0; e2 < 2; ++e2) {
       const int row = e2 * 8 + vh * 4 + (vj >> 2);   // plus multiples of 16
@@ -346,9 +346,9 @@ struct FragOffsets {
 };
 
 // S^T = K . Q^T for this wave's 32-key block(s) of the tile in `ktile`.
-template <int D, int KSPLIT>
+template <int D, int KSPLIT, int VREG = kVRegionOffset<D>()>
 __device__ __forceinline__ void qk_tile(const uint8_t *ktile, const bf16x8 (&qf)[D / 16],
-                                        f32x16 (&sacc)[2 / KSPLIT], const FragOffsets<D> &fo) {
+                                        f32x16 (&sacc)[2 / KSPLIT], const FragOffsets<D, VREG> &fo) {
   using Gm = TileGeom<D>;
   constexpr int NKS = D / 16, NKB = 2 / KSPLIT;
 #pragma unroll
@@ -456,12 +456,12 @@ constexpr int kFragAhead = 2;
 // exponentials, their bf16 packing and row sum, so the VALU works while the
 // matrix core runs.  sched_barrier fences keep that order through
 // scheduling.
-template <int D, int KSPLIT>
+template <int D, int KSPLIT, int VREG = kVRegionOffset<D>()>
 __device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf16x8 (&qf)[D / 16],
                                                  f32x16 (&s_next)[2 / KSPLIT],
                                                  f32x16 (&s_cur)[2 / KSPLIT],
                                                  bf16x8 (&pf)[4 / KSPLIT], Rows<D> &st, float c,
-                                                 float mc, const FragOffsets<D> &fo) {
+                                                 float mc, const FragOffsets<D, VREG> &fo) {
   using Gm = TileGeom<D>;
   constexpr int NKS = D / 16, NKB = 2 / KSPLIT;
   constexpr int NV = 16 * NKB;        // scores per lane
@@ -509,12 +509,12 @@ __device__ __forceinline__ void qk_next_with_exp(const uint8_t *ktile, const bf1
 // 16*(ps%2) + 8*e2 + 4h + (0..3), e2 = 0, 1; each half-fragment of V^T is one
 // transposing read: lane j of a 16-lane group points at 4 dims of key row
 // base + j/4, and receives 4 keys of dim d0 + (lane % 16).
-template <int D, int KSPLIT>
+template <int D, int KSPLIT, int VREG = kVRegionOffset<D>()>
 __device__ __forceinline__ void pv_tile(const uint8_t *vt, const bf16x8 (&pf)[4 / KSPLIT],
-                                        Rows<D> &st, int kh, const FragOffsets<D> &fo) {
+                                        Rows<D> &st, int kh, const FragOffsets<D, VREG> &fo) {
   using Gm = TileGeom<D>;
   constexpr int NDB = D / 32, NKB = 2 / KSPLIT;
-  const uint8_t *vbase = vt - kVRegionOffset<D>();   // fo.v holds the rest (and kh's rows)
+  const uint8_t *vbase = vt - VREG;   // fo.v holds the rest (and kh's rows)
   constexpr int NSTEP = 2 * NKB * NDB;
   // fragment n: k-step j2 = n / NDB (rows 32*(j2/2) + 16*(j2%2)), block db = n % NDB
   auto frag = [&](int n) {
@@ -541,13 +541,13 @@ __device__ __forceinline__ void pv_tile(const uint8_t *vt, const bf16x8 (&pf)[4 
 // lane's maximum over s_next (no masking) into tmax, one max3 per k-step
 // from the second on, so the VALU works while the matrix core runs and the
 // next step starts with only the lane-pair exchange left.
-template <int D, int KSPLIT>
+template <int D, int KSPLIT, int VREG = kVRegionOffset<D>()>
 __device__ __forceinline__ void pv_tile_max(const uint8_t *vt, const bf16x8 (&pf)[4 / KSPLIT],
-                                            Rows<D> &st, int kh, const FragOffsets<D> &fo,
+                                            Rows<D> &st, int kh, const FragOffsets<D, VREG> &fo,
                                             const f32x16 (&s_next)[2 / KSPLIT], float &tmax) {
   using Gm = TileGeom<D>;
   constexpr int NDB = D / 32, NKB = 2 / KSPLIT;
-  const uint8_t *vbase = vt - kVRegionOffset<D>();   // fo.v holds the rest (and kh's rows)
+  const uint8_t *vbase = vt - VREG;   // fo.v holds the rest (and kh's rows)
   constexpr int NSTEP = 2 * NKB * NDB;
   constexpr int NV = 16 * NKB;                      // scores per lane
   // scores per k-step (steps 1..NSTEP-1), even: two per v_max3_f32
@@ -730,10 +730,10 @@ __device__ __forceinline__ void token_block0_copy(uint8_t *sk, uint8_t *sv, cons
 // and V) against the wave's 32 query rows, as a 32-key tile whose scores
 // are masked block-diagonally: token i0 + i counts for a query row iff it
 // lies in [tok_lo, tok_hi), the row's own tokens (its beam's levels).
-template <int D, int KSPLIT>
+template <int D, int KSPLIT, int VREG = kVRegionOffset<D>()>
 __device__ __forceinline__ void token_block(Rows<D> &st, const bf16x8 (&qf)[D / 16],
                                             const uint8_t *kt, const uint8_t *vt,
-                                            const FragOffsets<D> &fo, int kh, int i0, int tok_lo,
+                                            const FragOffsets<D, VREG> &fo, int kh, int i0, int tok_lo,
                                             int tok_hi, float c, float thr, int lane) {
   static_assert(KSPLIT == 2, "a token block is one 32-key block per wave");
   using Gm = TileGeom<D>;
@@ -742,7 +742,7 @@ __device__ __forceinline__ void token_block(Rows<D> &st, const bf16x8 (&qf)[D / 
   const uint8_t *kb = kt - kh * 32 * Gm::RB;
   const uint8_t *vb = vt - kh * 32 * Gm::RB;
   f32x16 sb[1];
-  qk_tile<D, KSPLIT>(kb, qf, sb, fo);
+  qk_tile<D, KSPLIT, VREG>(kb, qf, sb, fo);
   const int base = i0 + 4 * hl - tok_lo;
   const uint32_t span = (uint32_t)max(tok_hi - tok_lo, 0);
 #pragma unroll
@@ -753,7 +753,7 @@ __device__ __forceinline__ void token_block(Rows<D> &st, const bf16x8 (&qf)[D / 
   bf16x8 pf[2];
   const float mc = softmax_max<D, KSPLIT, false>(sb, st, kh, 0, 0, 0, c, thr, lane);
   softmax_exp<D, KSPLIT>(sb, pf, st, c, mc);
-  pv_tile<D, KSPLIT>(vb, pf, st, kh, fo);
+  pv_tile<D, KSPLIT, VREG>(vb, pf, st, kh, fo);
 }
 
 // Online-softmax state of query row `ri` from the Unshared-stage partial
@@ -1393,15 +1393,433 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   }
 }
 
-template <int D, int RG, int KSPLIT>
-Bf16Geometry geometry_cfg(const DecodeParams &p) {
+// ---------------------------------------------------------------------------
+// The paired variant, for grids of at least two workgroups per compute unit.
+// One wave per row group of 32 query rows takes whole tiles of KT2 = 32
+// keys (no key halves, so no exchange of halves at the end), the tile ring
+// has NSTAGE2 = 4 stages, and the q rows and generated-token blocks pass
+// through ring stages, so a workgroup needs at most 80 KiB of LDS and two
+// of them share a compute unit.  The two waves on a SIMD then belong to
+// different workgroups: neither waits at the other's barrier, one's
+// softmax runs while the other's matrix products do, and one workgroup's
+// prologue and epilogue run under the other's tile loop.  The per-tile work
+// of a wave is the same as in decode_bf16_kernel (one 32-key block against
+// its 32 rows), done by the same helpers.
+constexpr int KT2 = 32;       // keys per tile
+constexpr int NSTAGE2 = 4;    // ring depth (tiles in flight = NSTAGE2 - 1)
+
+template <int D>
+constexpr int kPairedLdsBytes = 2 * NSTAGE2 * TileGeom<D, KT2>::TILE_BYTES;
+
+// One wave copies a whole generated-token block (32 rows of K to kt, of V
+// to vt, in the tile layout): block gb of the row block (TokenMap).
+template <int D, int RG>
+__device__ __forceinline__ void token_block_copy_wave(uint8_t *kt, uint8_t *vt,
+                                                      const uint16_t *ukg, const uint16_t *uvg,
+                                                      const TokenMap<RG> &tm, int gb, int lane) {
+  using Gm = TileGeom<D>;
+  constexpr int NQ = 32 * Gm::RB / 1024;  // 1 KiB copies per K (or V) block
+#pragma unroll
+  for (int qi = 0; qi < 2 * NQ; ++qi) {
+    const bool is_v = qi >= NQ;
+    const int q = is_v ? qi - NQ : qi;
+    const int row = q * Gm::ROWS_PER_COPY + lane / Gm::SLOTS;
+    const int64_t e = tm.row_elem(gb, row, D);
+    const uint8_t *src = reinterpret_cast<const uint8_t *>((is_v ? uvg : ukg) + e) +
+                         (((lane % Gm::SLOTS) ^ Gm::swz(row)) << 4);
+    dma16(src, (is_v ? vt : kt) + q * 1024);
+  }
+}
+
+// s_waitcnt lgkmcnt(0) alone (vmcnt and expcnt left at their maxima).
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+template <int D, int RG, bool TAPS>
+__global__ __launch_bounds__(RG * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_bf16_paired_kernel(DecodeParams p) {
+  constexpr int WAVES = RG;
+  constexpr int NT = WAVES * 64;
   constexpr int ROWS = RG * 32;
+  constexpr int NKS = D / 16;           // k-steps of the QK contraction
+  constexpr int NDB = D / 32;           // 32-row blocks of O^T
+  constexpr int KS = 2;                 // the helpers' unit: one 32-key block per wave
+  using Gm = TileGeom<D, KT2>;
+  constexpr int VREG = kVRegionOffset<D, KT2, NSTAGE2>();
+  constexpr int CPW = Gm::COPIES / WAVES;   // wave-wide copies per wave per tile
+  static_assert(RG <= NSTAGE2, "one ring stage per row group for its token blocks");
+  static_assert(32 * Gm::RB == Gm::TILE_BYTES && Gm::TILE_BYTES == NKS * 1024,
+                "a row group's 32 q rows (or token rows) fill one tile of NKS 1 KiB copies");
+
+  // K tiles of stages 0..3, then V tiles of stages 0..3
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[kPairedLdsBytes<D>];
+  // dynamic: ancestor slots [beams of the block][step + 1], then (when
+  // staged) the parent rows [step][BW] of levels 1..step
+  extern __shared__ int32_t dyn_lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int rg = __builtin_amdgcn_readfirstlane(tid >> 6);  // row group = wave
+  const int hl = lane >> 5;
+  const int ql = lane & 31;
+
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int rb = lb % p.n_rb;
+  const int split = (lb / p.n_rb) % p.n_split;
+  const int unit = lb / p.n_rb / p.n_split;
+  const int r = __builtin_amdgcn_readfirstlane(unit / p.Hkv);
+  const int k = unit % p.Hkv;
+  const int G = p.G, BW = p.BW, step = p.step;
+  const int L = clampi(p.prompt_len[r], 0, p.Lmax);
+  const float c = p.scale_log2;
+  const float thr = p.lazy_log2 / c;
+
+  const int row0 = rb * ROWS;
+  const int b_lo = row0 / G;
+  const int nb = (min(row0 + ROWS, p.M) - 1) / G - b_lo + 1;
+  int32_t *anc_lds = dyn_lds;
+  int32_t *par_lds = dyn_lds + nb * (step + 1);
+  const bool walk_here = p.anc == nullptr;
+  const bool staged = walk_here && p.stage_par != 0;
+
+#define XP_KT(S) (tiles + (S) * Gm::TILE_BYTES)
+#define XP_VT(S) (tiles + (NSTAGE2 + (S)) * Gm::TILE_BYTES)
+
+  // ---- copies that depend on nothing: the parent rows for the walk, and
+  // this wave's q rows, laid out like a tile (row-major, 16-byte slots
+  // permuted by swz) in ring stage 2 + rg / 2 (K buffer for even rg, V for
+  // odd); tiles 2 and 3 go there only after every wave holds its q.
+  const int32_t *par = p.parent_idx + (int64_t)r * p.S * BW;
+  if (staged) {
+    const int n_par = step * BW;
+    for (int c0 = rg * 64; c0 < n_par; c0 += WAVES * 64)
+      dma4(par + BW + min(c0 + lane, n_par - 1), par_lds + c0);
+  }
+  const uint16_t *qg = static_cast<const uint16_t *>(p.q);
+  uint16_t *og = static_cast<uint16_t *>(p.out);
+  const int row = row0 + rg * 32 + ql;
+  const bool valid = row < p.M;
+  const int rr = valid ? row : p.M - 1;
+  const int beam = rr / G;
+  const int64_t qoff = (((int64_t)r * BW + beam) * p.Hq + k * G + rr % G) * D;
+  uint8_t *qlds = (rg & 1) ? XP_VT(2 + rg / 2) : XP_KT(2 + rg / 2);
+#pragma unroll
+  for (int n = 0; n < NKS; ++n) {
+    const int qr = n * Gm::ROWS_PER_COPY + lane / Gm::SLOTS;   // row of the group
+    const int qrr = min(row0 + rg * 32 + qr, p.M - 1);
+    const int qb = qrr / G;
+    const int64_t qro = (((int64_t)r * BW + qb) * p.Hq + k * G + (qrr - qb * G)) * D;
+    dma16<false>(qg + qro + (((lane % Gm::SLOTS) ^ Gm::swz(qr)) << 3), qlds + n * 1024);
+  }
+
+  const uint16_t *ukg = static_cast<const uint16_t *>(p.unshared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  const uint16_t *uvg = static_cast<const uint16_t *>(p.unshared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.S * BW * D;
+  const uint16_t *skg = static_cast<const uint16_t *>(p.shared_k) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  const uint16_t *svg = static_cast<const uint16_t *>(p.shared_v) +
+                        ((int64_t)r * p.Hkv + k) * p.Lmax * D;
+  CopyPlan<D, WAVES, KT2> cplan;
+  cplan.init(rg, lane);
+  // tiles 0 and 1 (keys [0, 2 KT2)) before the prompt length is known: they
+  // are right whenever the prompt has more than two tiles
+  const bool speculate = p.n_split == 1 && p.Lmax >= 2 * KT2;
+  if (speculate) {
+    tile_copy<D, WAVES, false, false, KT2>(XP_KT(0), XP_VT(0), cplan, skg, svg, 0, 0, rg);
+    tile_copy<D, WAVES, false, false, KT2>(XP_KT(1), XP_VT(1), cplan, skg, svg, KT2, 0, rg);
+  }
+  // the prompt's tiles split evenly over the key splits: this workgroup
+  // takes tiles [t_base, t_base + n_tiles); the last window of the prompt
+  // is shifted back to end at L (its keys already counted get masked)
+  const int n_tiles_all = (L + KT2 - 1) / KT2;
+  const int t_base = split * n_tiles_all / p.n_split;
+  const int n_tiles = (split + 1) * n_tiles_all / p.n_split - t_base;
+  const int last_key0 = L >= KT2 ? L - KT2 : 0;
+#define XP_KEY0(T) (t_base + (T) + 1 < n_tiles_all ? (t_base + (T)) * KT2 : last_key0)
+  const bool spec_ok = speculate && n_tiles > 2;
+
+  // ---- the parent rows and q are in (older than the speculative tiles);
+  // walk the ancestor chains of the block's beams, take q into registers
+  if (speculate)
+    wait_vm_lgkm0<2 * CPW>();
+  else
+    wait_vm_lgkm0<0>();
+  lds_barrier();   // every wave's parent and q copies have landed
+  if (walk_here) {
+    for (int i = tid; i < nb; i += NT) {
+      int a = b_lo + i;
+      int32_t *dst = anc_lds + i * (step + 1);
+      dst[step] = a;
+      for (int t = step; t >= 1; --t) {
+        a = clampi(staged ? par_lds[(t - 1) * BW + a] : par[(int64_t)t * BW + a], 0, BW - 1);
+        dst[t - 1] = a;
+      }
+    }
+  }
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8 *>(qlds + ql * Gm::RB +
+                                                (((2 * ks + hl) ^ Gm::swz(ql)) << 4));
+  wait_lgkm0();
+  lds_barrier();   // the ancestor slots are visible; every wave holds its q
+  if (!spec_ok) {
+    if (speculate) wait_vm_lgkm0<0>();   // before stages 0 and 1 are written again
+    if (n_tiles > 0) {
+      if (L < KT2)
+        tile_copy<D, WAVES, true, false, KT2>(XP_KT(0), XP_VT(0), cplan, skg, svg, 0, L, rg);
+      else
+        tile_copy<D, WAVES, false, false, KT2>(XP_KT(0), XP_VT(0), cplan, skg, svg, XP_KEY0(0),
+                                               L, rg);
+    }
+    if (n_tiles > 1)
+      tile_copy<D, WAVES, false, false, KT2>(XP_KT(1), XP_VT(1), cplan, skg, svg, XP_KEY0(1), L,
+                                             rg);
+  }
+  if (n_tiles > 2)
+    tile_copy<D, WAVES, false, false, KT2>(XP_KT(2), XP_VT(2), cplan, skg, svg, XP_KEY0(2), L, rg);
+
+  // st: the online-softmax state of the row; with TAPS, of the Shared stage
+  // alone, and su that of the Unshared stage
+  Rows<D> st, su;
+  st.clear();
+  su.clear();
+  if (!walk_here) {
+    // deep chains: the Unshared stage was computed beforehand, one workgroup
+    // per (request, beam, KV head); key split 0 starts from its partial
+    if (split == 0) {
+      if constexpr (TAPS)
+        seed_rows<D>(su, p, qoff / D, hl);
+      else
+        seed_rows<D>(st, p, qoff / D, hl);
+    }
+    // complete these compiler-counted loads before the tile loop (see the
+    // same step in decode_bf16_kernel)
+    wait_vm_lgkm0<0>();
+  }
+
+  // ---- tile 0 is in once all but the copies younger than it are
+  if (n_tiles > 2)
+    wait_vm_lgkm0<2 * CPW>();
+  else if (n_tiles > 1)
+    wait_vm_lgkm0<CPW>();
+  else
+    wait_vm_lgkm0<0>();
+  lds_barrier();   // tile 0 is visible
+
+  // ---- Shared stage.  Per tile t (in stage t % 4) but the last: wait for
+  // tile t + 1 and synchronise, finish the row maxima of tile t, issue the
+  // S^T MFMAs of tile t + 1 interleaved with the exponentials of tile t,
+  // then tile t's PV MFMAs (with tile t + 1's row maxima between them),
+  // then copy tile t + 3 into the stage tile t - 1 used.
+  FragOffsets<D, VREG> fo;
+  fo.init(0, 1, lane);
+  f32x16 s_cur[1], s_next[1];
+  bf16x8 pf[2];
+  if (n_tiles > 0) qk_tile<D, KS, VREG>(XP_KT(0), qf, s_cur, fo);
+  float tmax_cur = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) tmax_cur = fmaxf(tmax_cur, s_cur[0][e]);
+#define XP_TILE_STEP(ST)                                                              \
+  {                                                                                   \
+    const int t = t0 + (ST);                                                          \
+    if (t + 1 >= n_tiles) break;                                                      \
+    /* tile t + 1 is in once all but the copy younger than it (tile t + 2, */         \
+    /* copied at step t - 1 or, for t = 0, in the prologue) are */                   \
+    if (t + 2 < n_tiles)                                                              \
+      wait_vm_lgkm0<CPW>();                                                           \
+    else                                                                              \
+      wait_vm_lgkm0<0>();                                                             \
+    lds_barrier();                                                                    \
+    const float mc = softmax_max_finish<D>(tmax_cur, st, c, thr);                     \
+    qk_next_with_exp<D, KS, VREG>(XP_KT(((ST) + 1) % NSTAGE2), qf, s_next, s_cur, pf, st, \
+                                  c, mc, fo);                                         \
+    pv_tile_max<D, KS, VREG>(XP_VT(ST), pf, st, 0, fo, s_next, tmax_cur);             \
+    if (t + 3 < n_tiles)                                                              \
+      tile_copy<D, WAVES, false, true, KT2>(XP_KT(((ST) + 3) % NSTAGE2),              \
+                                            XP_VT(((ST) + 3) % NSTAGE2), cplan, skg, svg, \
+                                            XP_KEY0(t + 3), L, rg);                   \
+    s_cur[0] = s_next[0];                                                             \
+  }
+  static_assert(NSTAGE2 == 4, "the tile loop below is unrolled for 4 stages");
+  for (int t0 = 0; t0 + 1 < n_tiles; t0 += NSTAGE2) {
+    XP_TILE_STEP(0)
+    XP_TILE_STEP(1)
+    XP_TILE_STEP(2)
+    XP_TILE_STEP(3)
+  }
+#undef XP_TILE_STEP
+  if (n_tiles > 0) {  // the last tile: every copy has landed
+    const int t = n_tiles - 1;
+    const int lo = (t_base + t) * KT2;   // keys below were counted by earlier tiles
+    const int key0 = XP_KEY0(t);         // first key the tile holds
+    const bool masked = key0 < lo || key0 + KT2 > L;
+    const float mc = masked ? softmax_max<D, KS, true>(s_cur, st, 0, key0, lo, L, c, thr, lane)
+                            : softmax_max<D, KS, false>(s_cur, st, 0, key0, lo, L, c, thr, lane);
+    softmax_exp<D, KS>(s_cur, pf, st, c, mc);
+    pv_tile<D, KS, VREG>(XP_VT(t % NSTAGE2), pf, st, 0, fo);
+  }
+#undef XP_KEY0
+
+  wait_vm_lgkm0<0>();
+  lds_barrier();   // every wave is done with the ring
+  if (p.anc_out && walk_here && k == 0 && split == 0) {
+    // the ancestor slots this workgroup walked, for the beams whose first
+    // query row lies in its block: anc_out [R][step + 1][BW]
+    const int bf = (row0 + G - 1) / G;
+    const int n = (min(row0 + ROWS, p.M) + G - 1) / G - bf;
+    for (int i = tid; i < n * (step + 1); i += NT) {
+      const int bi = i / (step + 1), t = i - bi * (step + 1);
+      p.anc_out[((int64_t)r * (step + 1) + t) * BW + bf + bi] =
+          anc_lds[(bf - b_lo + bi) * (step + 1) + t];
+    }
+  }
+
+  // ---- Unshared stage from the generated-token rows, on the matrix cores:
+  // row group rg's tokens (its beams' levels, TokenMap) in blocks of 32
+  // rows, each gathered by the wave into its own ring stage and contracted
+  // like a 32-key tile under a block-diagonal mask, into the same state
+  // (with TAPS, into su)
+  if (walk_here) {
+    const int nlev = step + 1;
+    const int nbr_max = (32 % G == 0) ? 32 / G : 32 / G + 2;  // beams 32 rows can touch
+    const int n_blk = (nbr_max * nlev + 31) / 32;
+    TokenMap<RG> tmap;
+    tmap.init(anc_lds, n_blk, nlev, BW, nb, G, row0, b_lo);
+    const int grow = row0 + rg * 32;
+    const int gfirst = grow / G;
+    const int n_valid = max(0, min((grow + 31) / G, BW - 1) - gfirst + 1) * nlev;
+    const int tok_lo = ((grow + ql) / G - gfirst) * nlev;
+    const int tok_hi = min(tok_lo + nlev, n_valid);
+#pragma unroll 1
+    for (int b = 0; b < n_blk; ++b) {
+      token_block_copy_wave<D, RG>(XP_KT(rg), XP_VT(rg), ukg, uvg, tmap, b * RG + rg, lane);
+      wait_vm_lgkm0<0>();   // this wave's own copies: no other wave uses stage rg now
+      if constexpr (TAPS)
+        token_block<D, KS, VREG>(su, qf, XP_KT(rg), XP_VT(rg), fo, 0, 32 * b, tok_lo, tok_hi, c,
+                                 thr, lane);
+      else
+        token_block<D, KS, VREG>(st, qf, XP_KT(rg), XP_VT(rg), fo, 0, 32 * b, tok_lo, tok_hi, c,
+                                 thr, lane);
+    }
+  }
+
+  // ---- Merge / epilogue
+  const int64_t n_rows_all = (int64_t)p.R * BW * p.Hq;
+  const int64_t ri = qoff / D;
+  if constexpr (!TAPS) {
+    if (p.n_split > 1) {
+      // one key split's partial (m, l, unnormalised O); merge_splits_kernel
+      // combines the splits and writes out
+      if (!valid) return;
+      const int64_t pr = split * n_rows_all + ri;
+      const float lt = pair_sum(st.l);
+      if (hl == 0) {
+        p.part_ml[pr * 2 + 0] = st.m;
+        p.part_ml[pr * 2 + 1] = lt;
+      }
+      float *po = p.part_o + pr * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4 *>(po + db * 32 + 8 * j + 4 * hl) =
+              make_float4(st.O[db][4 * j], st.O[db][4 * j + 1], st.O[db][4 * j + 2],
+                          st.O[db][4 * j + 3]);
+      return;
+    }
+    // the row group's 32 normalised rows as bf16 in the wave's own K stage
+    // (row-major, 16-byte slots permuted by swz), then stored whole, 16
+    // bytes per lane
+    const float lt = pair_sum(st.l);
+    const float inv = 1.f / lt;
+    if (valid && p.lse && hl == 0) p.lse[ri] = st.m * p.scale + __logf(lt);
+    uint8_t *ost = XP_KT(rg);
+    const int osw = Gm::swz(ql);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x4 pk = {(__bf16)(st.O[db][4 * j + 0] * inv), (__bf16)(st.O[db][4 * j + 1] * inv),
+                           (__bf16)(st.O[db][4 * j + 2] * inv), (__bf16)(st.O[db][4 * j + 3] * inv)};
+        *reinterpret_cast<bf16x4 *>(ost + ql * Gm::RB + (((4 * db + j) ^ osw) << 4) + hl * 8) = pk;
+      }
+    wait_lgkm0();
+    constexpr int NCH = 32 * Gm::SLOTS / 64;   // store instructions per wave
+#pragma unroll
+    for (int n = 0; n < NCH; ++n) {
+      const int idx = n * 64 + lane;
+      const int orow = idx / Gm::SLOTS, ch = idx % Gm::SLOTS;
+      const uint4 v =
+          *reinterpret_cast<const uint4 *>(ost + orow * Gm::RB + ((ch ^ Gm::swz(orow)) << 4));
+      const int grr = row0 + rg * 32 + orow;
+      if (grr < p.M) {
+        const int gb = grr / G;
+        const int64_t go = (((int64_t)r * BW + gb) * p.Hq + k * G + (grr - gb * G)) * D;
+        // written once: past the caches (non-temporal)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                    reinterpret_cast<u32x4 *>(og + go + ch * 8));
+      }
+    }
+  } else {
+    // the Shared partial (m, l, O) and the Unshared partial, each on its
+    // own, then their explicit OnlineSoftmax merge
+    const float ls = pair_sum(st.l), lu = pair_sum(su.l);
+    const float ms = st.m, mu = su.m;
+    const float inv_s = ls > 0.f ? 1.f / ls : 0.f;
+    const float inv_u = 1.f / lu;
+    const float mm = fmaxf(ms, mu);
+    const float ws = ls > 0.f ? ls * __builtin_amdgcn_exp2f((ms - mm) * c) : 0.f;
+    const float wu = lu * __builtin_amdgcn_exp2f((mu - mm) * c);
+    const float inv_z = 1.f / (ws + wu);
+    if (!valid) return;
+    if (p.stage_ml && hl == 0) {
+      p.stage_ml[ri * 2 + 0] = ls > 0.f ? ms * p.scale : -INFINITY;
+      p.stage_ml[ri * 2 + 1] = ls;
+      p.stage_ml[(n_rows_all + ri) * 2 + 0] = mu * p.scale;
+      p.stage_ml[(n_rows_all + ri) * 2 + 1] = lu;
+    }
+    if (p.stage_o) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int d = db * 32 + 8 * (e / 4) + 4 * hl + e % 4;
+          p.stage_o[ri * D + d] = st.O[db][e] * inv_s;
+          p.stage_o[(n_rows_all + ri) * D + d] = su.O[db][e] * inv_u;
+        }
+    }
+    if (p.lse && hl == 0) p.lse[ri] = mm * p.scale + __logf(ws + wu);
+    uint16_t *op = og + qoff;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const f32x16 o = (st.O[db] * (inv_s * ws) + su.O[db] * (inv_u * wu)) * inv_z;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x4 pk = {(__bf16)o[4 * j + 0], (__bf16)o[4 * j + 1], (__bf16)o[4 * j + 2],
+                           (__bf16)o[4 * j + 3]};
+        *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * j + 4 * hl) = pk;
+      }
+    }
+  }
+#undef XP_KT
+#undef XP_VT
+}
+
+// Launch geometry of one variant: `threads` per workgroup of `rows` query
+// rows, `static_lds` bytes of static LDS, and at most `budget` bytes of LDS
+// per workgroup (the paired variant keeps two workgroups per CU).
+Bf16Geometry geometry_for(const DecodeParams &p, int rows, int threads, int static_lds,
+                          int budget, bool paired) {
   Bf16Geometry g{};
-  g.rows = ROWS;
-  g.threads = RG * KSPLIT * 64;
-  g.grid = (int64_t)p.R * p.Hkv * ((p.M + ROWS - 1) / ROWS) * p.n_split;
-  g.static_lds = kTilesLdsBytes<D>;
-  g.beams_per_block = beams_per_block(ROWS, p.G, p.BW);
+  g.rows = rows;
+  g.threads = threads;
+  g.paired = paired;
+  g.grid = (int64_t)p.R * p.Hkv * ((p.M + rows - 1) / rows) * p.n_split;
+  g.static_lds = static_lds;
+  g.beams_per_block = beams_per_block(rows, p.G, p.BW);
   g.dyn_lds = 0;
   g.stage_par = false;
   if (p.anc == nullptr) {
@@ -1410,7 +1828,7 @@ Bf16Geometry geometry_cfg(const DecodeParams &p) {
     // parent rows, copied 64 ints per wave instruction: whole rounds of 64
     const int par_bytes = (p.step * p.BW + 63) / 64 * 64 * (int)sizeof(int32_t);
     if (p.step > 0 && (int64_t)p.step * p.BW <= kParentLdsInts &&
-        g.static_lds + g.dyn_lds + par_bytes <= kLdsLimit) {
+        g.static_lds + g.dyn_lds + par_bytes <= budget) {
       g.stage_par = true;
       g.dyn_lds += par_bytes;
     }
@@ -1418,42 +1836,60 @@ Bf16Geometry geometry_cfg(const DecodeParams &p) {
   return g;
 }
 
-template <int D, int RG, int KSPLIT, bool TAPS>
-hipError_t launch_cfg(const DecodeParams &p0, hipStream_t stream, LaunchEvents ev) {
-  constexpr int ROWS = RG * 32;
+// Rows per workgroup: 32 (1 row group) or 64 (2) for few query rows per
+// (request, KV head); otherwise 128 rows in 4 row groups.
+int rows_per_block(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : 128); }
+
+// Workgroups of the paired variant that keep every compute unit's two
+// slots busy (256 CUs).
+constexpr int64_t kPairedMinGrid = 512;
+
+template <int D>
+Bf16Geometry geometry_d(const DecodeParams &p) {
+  const int rows = rows_per_block(p.M);
+  if (rows == 128) {
+    const Bf16Geometry g = geometry_for(p, 128, 4 * 64, kPairedLdsBytes<D>, kLdsLimit / 2, true);
+    if (g.grid >= kPairedMinGrid && g.static_lds + g.dyn_lds <= kLdsLimit / 2) return g;
+  }
+  return geometry_for(p, rows, rows / 32 * 2 * 64, kTilesLdsBytes<D>, kLdsLimit, false);
+}
+
+template <int D, int RG, bool TAPS>
+hipError_t launch_cfg(const DecodeParams &p0, const Bf16Geometry &g, hipStream_t stream,
+                      LaunchEvents ev) {
   DecodeParams p = p0;
-  p.n_rb = (p.M + ROWS - 1) / ROWS;
+  p.n_rb = (p.M + g.rows - 1) / g.rows;
   if (TAPS && p.n_split != 1) return hipErrorInvalidValue;
-  const Bf16Geometry g = geometry_cfg<D, RG, KSPLIT>(p);
   if (g.grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (g.static_lds + g.dyn_lds > kLdsLimit) return hipErrorInvalidConfiguration;
+  if (g.static_lds + g.dyn_lds > (g.paired ? kLdsLimit / 2 : kLdsLimit))
+    return hipErrorInvalidConfiguration;
   p.stage_par = g.stage_par ? 1 : 0;
   const uint32_t dyn = (uint32_t)g.dyn_lds;
+  auto kernel = decode_bf16_kernel<D, RG, 2, TAPS>;
+  if constexpr (RG == 4) {
+    if (g.paired) kernel = decode_bf16_paired_kernel<D, RG, TAPS>;
+  } else if (g.paired) {
+    return hipErrorInvalidConfiguration;   // the paired variant runs 128-row workgroups only
+  }
   if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)g.grid),
-                          dim3(g.threads), dyn, stream, ev.start, ev.stop, 0u, p);
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)g.grid), dim3(g.threads), dyn, stream, ev.start,
+                          ev.stop, 0u, p);
   else
-    hipLaunchKernelGGL((decode_bf16_kernel<D, RG, KSPLIT, TAPS>), dim3((unsigned)g.grid),
-                       dim3(g.threads), dyn, stream, p);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)g.grid), dim3(g.threads), dyn, stream, p);
   return hipGetLastError();
 }
 
-// Rows per workgroup: 32 (1 row group) or 64 (2) for few query rows per
-// (request, KV head); otherwise 128 rows in 4 row groups.  Always two key
-// halves.
-int rows_per_block(int M) { return M <= 32 ? 32 : (M <= 64 ? 64 : 128); }
-
 template <int D>
 hipError_t launch_d(const DecodeParams &p, bool taps, hipStream_t stream, LaunchEvents ev) {
-  const int rows = rows_per_block(p.M);
+  const Bf16Geometry g = geometry_d<D>(p);
   if (taps) {
-    if (rows == 32) return launch_cfg<D, 1, 2, true>(p, stream, ev);
-    if (rows == 64) return launch_cfg<D, 2, 2, true>(p, stream, ev);
-    return launch_cfg<D, 4, 2, true>(p, stream, ev);
+    if (g.rows == 32) return launch_cfg<D, 1, true>(p, g, stream, ev);
+    if (g.rows == 64) return launch_cfg<D, 2, true>(p, g, stream, ev);
+    return launch_cfg<D, 4, true>(p, g, stream, ev);
   }
-  if (rows == 32) return launch_cfg<D, 1, 2, false>(p, stream, ev);
-  if (rows == 64) return launch_cfg<D, 2, 2, false>(p, stream, ev);
-  return launch_cfg<D, 4, 2, false>(p, stream, ev);
+  if (g.rows == 32) return launch_cfg<D, 1, false>(p, g, stream, ev);
+  if (g.rows == 64) return launch_cfg<D, 2, false>(p, g, stream, ev);
+  return launch_cfg<D, 4, false>(p, g, stream, ev);
 }
 
 // Merge of the key splits' partials (OnlineSoftmax over the splits, the
@@ -1514,15 +1950,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(DecodeParams p) {
 int bf16_rows_per_block(const DecodeParams &p) { return rows_per_block(p.M); }
 
 Bf16Geometry bf16_geometry(const DecodeParams &p) {
-  const int rows = rows_per_block(p.M);
-  if (p.D == 64) {
-    if (rows == 32) return geometry_cfg<64, 1, 2>(p);
-    if (rows == 64) return geometry_cfg<64, 2, 2>(p);
-    return geometry_cfg<64, 4, 2>(p);
-  }
-  if (rows == 32) return geometry_cfg<128, 1, 2>(p);
-  if (rows == 64) return geometry_cfg<128, 2, 2>(p);
-  return geometry_cfg<128, 4, 2>(p);
+  return p.D == 64 ? geometry_d<64>(p) : geometry_d<128>(p);
 }
 
 hipError_t launch_merge_splits_bf16(const DecodeParams &p, hipStream_t stream, LaunchEvents ev) {

@@ -180,6 +180,7 @@ struct Bf16Geometry {
   int dyn_lds;         // bytes of dynamic LDS
   int beams_per_block; // most beams one workgroup's rows touch
   bool stage_par;      // parent rows staged in LDS for the in-kernel walk
+  bool paired;         // the variant two workgroups of which share a compute unit
 };
 // LDS one workgroup may use (gfx950: 160 KiB per compute unit).
 constexpr int kLdsLimit = 160 * 1024;

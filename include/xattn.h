@@ -291,9 +291,15 @@ xattn_status xattn_reorder_unshared_timed(const xattn_shape *shape, void *unshar
  * GPU).  xattn_decode follows exactly this plan.
  */
 typedef enum {
-  XATTN_KERNEL_STAGED_BF16 = 0,  /* bf16: the staged MFMA kernel */
-  XATTN_KERNEL_F32 = 1,          /* float32: one workgroup per query row */
-  XATTN_KERNEL_PER_BEAM_BF16 = 2 /* bf16 with <= 8 query rows per request and KV head */
+  XATTN_KERNEL_STAGED_BF16 = 0,   /* bf16: the staged MFMA kernel, one workgroup per
+                                     compute unit, two waves per 32 query rows (one
+                                     per half of each 64-key tile) */
+  XATTN_KERNEL_F32 = 1,           /* float32: one workgroup per query row */
+  XATTN_KERNEL_PER_BEAM_BF16 = 2, /* bf16 with <= 8 query rows per request and KV head */
+  XATTN_KERNEL_STAGED_BF16_PAIRED = 3 /* bf16, grids of >= 512 workgroups of 128 rows:
+                                     the same stages with one wave per 32 query rows on
+                                     32-key tiles, <= 80 KiB of LDS, two workgroups per
+                                     compute unit */
 } xattn_kernel;
 
 typedef struct {

@@ -18,6 +18,7 @@ import torch
 
 import oracle
 import generative_recommendation_beam_xattn_amd as X
+from generative_recommendation_beam_xattn_amd import binding as B
 from generative_recommendation_beam_xattn_amd import workloads as W
 from tests.gpu_util import TOL, DeviceWorkload, host_args, sample_rows, to_dev, to_f64, workload
 
@@ -82,6 +83,31 @@ def test_small_shapes(name, dtype):
     kw = dict(SMALL[name])
     w = W.custom(name=name, seed=zlib.crc32(name.encode()) % 1000, dtype=dtype, **kw)
     check_full(w, name + "/" + dtype)
+
+
+# Shapes that take the paired variant (>= 512 workgroups of 128 query
+# rows): prompt lengths through every 32-key tile boundary (0, 1, one
+# tile, one key past it, two and three tiles, ...), D = 128 and 64, one head
+# per KV head with the LDS full, a deep chain, and G = 3 (row blocks that
+# split a beam)
+_EDGES = [0, 1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 128, 200, 257, 300, 511]
+PAIRED = {
+    "paired_ragged": dict(R=64, BW=40, Hq=16, Hkv=8, D=128, L=_EDGES * 4, steps=[0, 2], S=3),
+    "paired_d64": dict(R=64, BW=40, Hq=16, Hkv=8, D=64, L=_EDGES * 4, steps=[1], S=2),
+    "paired_g1_full_lds": dict(R=32, BW=136, Hq=8, Hkv=8, D=128, L=(40, 130), steps=[15],
+                               S=16),
+    "paired_g3": dict(R=64, BW=50, Hq=24, Hkv=8, D=128, L=(60, 200), steps=[2], S=3),
+    "paired_deep_chain": dict(R=64, BW=40, Hq=16, Hkv=8, D=128, L=(0, 150), steps=[20], S=21),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAIRED))
+def test_paired_variant_shapes(name):
+    w = W.custom(name=name, seed=zlib.crc32(name.encode()) % 1000, dtype="bf16", **PAIRED[name])
+    shape = B.Shape(w.R, w.BW, w.Hq, w.Hkv, w.D, w.Lmax, w.S, B.XATTN_BF16, 0.0)
+    for s in w.steps:
+        assert X.plan(shape, s).kernel == B.KERNEL_STAGED_BF16_PAIRED
+    check_full(w, name)
 
 
 def test_tiny_workload_all_steps():
@@ -210,6 +236,9 @@ DEBUG = {
     # empty prompt, 128 beams, 4 query heads per KV head
     "bf16_serving_tiling": dict(R=3, BW=128, Hq=16, Hkv=4, D=128, L=[700, 0, 257], steps=[2]),
     "bf16_segmented_deep": dict(R=1, BW=40, Hq=4, Hkv=2, D=128, L=[100], steps=[150], S=151),
+    # the paired variant (512 workgroups of 128 rows), short and deep chains
+    "bf16_paired": dict(R=64, BW=40, Hq=16, Hkv=8, D=128, L=_EDGES * 4, steps=[2]),
+    "bf16_paired_deep": dict(R=64, BW=40, Hq=16, Hkv=8, D=128, L=(0, 150), steps=[20], S=21),
     "f32_ragged": dict(R=2, BW=5, Hq=8, Hkv=2, D=128, L=[0, 130], steps=[2], dtype="f32"),
 }
 

@@ -46,23 +46,36 @@ def test_lds_fits_and_beam_bound_holds_over_the_shape_space(D):
         if BW * G <= 8:
             assert pl.kernel == B.KERNEL_PER_BEAM_BF16
             continue
-        assert pl.kernel == B.KERNEL_STAGED_BF16
-        assert pl.kernels == 1 and pl.ancestor_walk == 0 and pl.workspace_bytes == 0
-        assert pl.lds_bytes <= LDS_LIMIT, (G, BW, step, D, pl.lds_bytes)
         rows = pl.rows_per_block
         assert rows == (32 if BW * G <= 32 else 64 if BW * G <= 64 else 128)
+        assert pl.kernels == 1 and pl.ancestor_walk == 0 and pl.workspace_bytes == 0
         exact = brute_beams_per_block(BW, G, rows)
         assert exact <= pl.beams_per_block <= BW
         if rows % G == 0:
             assert pl.beams_per_block == min(rows // G, BW) == exact
         # parent rows are staged whenever they hold at most 2048 ints and fit
         want = 0 < step and step * BW <= 2048
-        static = 2 * 4 * 64 * 2 * D + 2 * 32 * 2 * D
         dyn = pl.beams_per_block * (step + 1) * 4
         par = -(-step * BW // 64) * 64 * 4
-        fits = static + dyn + par <= LDS_LIMIT
-        assert pl.parents_in_lds == int(want and fits)
-        assert pl.lds_bytes == static + dyn + (par if pl.parents_in_lds else 0)
+        grid = 2 * -(-BW * G // rows)                       # 2 requests x 1 KV head
+        assert pl.grid == grid
+        # >= 512 workgroups of 128 rows take the paired variant, whose LDS
+        # fits twice per CU; otherwise one workgroup per CU
+        pstatic = 2 * 4 * 32 * 2 * D
+        paired = rows == 128 and grid >= 512 and pstatic + dyn <= LDS_LIMIT // 2
+        if paired:
+            assert pl.kernel == B.KERNEL_STAGED_BF16_PAIRED, (G, BW, step, D)
+            assert pl.threads_per_block == 256
+            staged = want and pstatic + dyn + par <= LDS_LIMIT // 2
+            assert pl.parents_in_lds == int(staged)
+            assert pl.lds_bytes == pstatic + dyn + (par if staged else 0) <= LDS_LIMIT // 2
+        else:
+            assert pl.kernel == B.KERNEL_STAGED_BF16, (G, BW, step, D)
+            assert pl.threads_per_block == rows // 32 * 2 * 64
+            static = 2 * 4 * 64 * 2 * D + 2 * 32 * 2 * D
+            staged = want and static + dyn + par <= LDS_LIMIT
+            assert pl.parents_in_lds == int(staged)
+            assert pl.lds_bytes == static + dyn + (par if staged else 0) <= LDS_LIMIT
         checked += 1
     assert checked > 3000
 
@@ -74,6 +87,11 @@ def test_widest_single_head_groups_fill_lds_exactly():
     assert pl.rows_per_block == 128 and pl.beams_per_block == 128
     assert pl.parents_in_lds == 1
     assert pl.lds_bytes == LDS_LIMIT
+    # the paired variant: 65536 + 8192 + 8192 bytes, exactly half
+    pl = B.plan(shape(num_requests=32, beam_width=136, num_q_heads=8, num_kv_heads=8), 15)
+    assert pl.kernel == B.KERNEL_STAGED_BF16_PAIRED and pl.grid == 512
+    assert pl.parents_in_lds == 1
+    assert pl.lds_bytes == LDS_LIMIT // 2
 
 
 def test_workload_plans():
@@ -84,9 +102,14 @@ def test_workload_plans():
         for step in steps:
             pl = B.plan(shape(num_requests=R, beam_width=BW, num_q_heads=Hq, num_kv_heads=Hkv,
                               max_prompt_len=L, max_steps=S), step)
-            assert (pl.kernel, pl.kernels, pl.key_splits, pl.rows_per_block) == (0, 1, 1, 128)
+            # serving: 256 workgroups, one per CU with two waves per row group;
+            # large batch and wide beam: 4096 and 1024, two per CU (paired)
+            paired = R * Hkv * BW * (Hq // Hkv) // 128 >= 512
+            assert pl.kernel == (B.KERNEL_STAGED_BF16_PAIRED if paired else B.KERNEL_STAGED_BF16)
+            assert (pl.kernels, pl.key_splits, pl.rows_per_block) == (1, 1, 128)
             assert pl.grid == R * Hkv * BW * (Hq // Hkv) // 128
-            assert pl.threads_per_block == 512
+            assert pl.threads_per_block == (256 if paired else 512)
+            assert pl.lds_bytes <= (LDS_LIMIT // 2 if paired else LDS_LIMIT)
     # the prefix sweep: 512 levels (segmented walk), the Unshared stage first,
     # key splits where the grid is small; one sequence per group runs per beam
     for G, kernels, splits in [(1, 3, 1), (8, 4, 1), (32, 5, 4), (256, 5, 4)]:
