@@ -261,9 +261,9 @@ def valid_mask_leg(w, steps: int, dev, stream) -> dict | None:
     0 and 1, sparse at 2), at every depth, on logits rotated through enough
     buffers (>= 512 MB) to come from HBM.  Beams sit on prefixes of random
     items (one in ten random, mostly dead).  Algorithmic bytes per launch:
-    4 B per slot that becomes -inf, 16 B read per 4-slot group that mixes
-    valid and invalid slots, and each distinct node's mask row (dense) or
-    children (sparse) once."""
+    4 B per slot that becomes -inf (valid slots are neither read nor
+    written), and each distinct node's mask row (dense) or children (sparse)
+    once."""
     import torch
     from generative_recommendation_beam_xattn_amd import binding as B
     from generative_recommendation_beam_xattn_amd import workloads as W
@@ -294,16 +294,14 @@ def valid_mask_leg(w, steps: int, dev, stream) -> dict | None:
             vp.mask(depth, node, bufs[k % n_buf], stream=stream, events=ev[k])
         torch.cuda.synchronize()
         us = float(np.mean([a.elapsed_time(b) for a, b in ev[1:]]) * 1e3)
-        fin = torch.isfinite(bufs[0]).view(R * BW, V // 4, 4).sum(dim=2).cpu().numpy()
-        n_valid = int(fin.sum())
-        mixed = int(np.sum((fin > 0) & (fin < 4)))
+        n_valid = int(torch.isfinite(bufs[0]).sum().item())
         nodes = np.unique(node.cpu().numpy())
         nodes = nodes[nodes >= 0]
         if depth < vp.layout.dense_levels:
             table_bytes = len(nodes) * vp.layout.words * 4
         else:
             table_bytes = 8 * len(nodes) + 4 * n_valid
-        byts = 4 * (R * BW * V - n_valid) + 16 * mixed + table_bytes
+        byts = 4 * (R * BW * V - n_valid) + table_bytes
         out.append({"depth": depth, "dense": depth < vp.layout.dense_levels, "kernel_us": us,
                     "valid_slots": n_valid, "bytes": byts, "GBps": byts / us / 1e3,
                     "frac_of_hbm_peak": byts / us / 1e3 / HBM_PEAK_GBS})

@@ -16,7 +16,7 @@
 // Kernels.  valid_mask_kernel masks one logits row per workgroup in place:
 // the row's bitmap, in LDS, is the node's dense bit row (early depths) or is
 // built from the node's children (later depths), and only invalid entries are
-// written (-inf); valid ones are not touched.  trie_advance_kernel moves
+// written (-inf); valid ones are neither read nor written.  trie_advance_kernel moves
 // every new beam to the child of its parent's node through its new token
 // (-1 when the path leaves the vocabulary).
 #include <hip/hip_ext.h>
@@ -31,12 +31,8 @@
 namespace xattn {
 namespace {
 
-// masked logits are written once, past the caches (non-temporal stores);
-// the loads stay cached: groups that need no read all load the row's start
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
+// masked logits are written once, past the caches (non-temporal stores)
 constexpr int kMaskThreads = 256;
-constexpr int kMaskBatch = 8;   // groups of 4 tokens a thread has in flight
 constexpr int kAdvanceThreads = 256;
 
 __device__ inline const int32_t *i32_at(const uint8_t *base, int64_t off) {
@@ -44,7 +40,7 @@ __device__ inline const int32_t *i32_at(const uint8_t *base, int64_t off) {
 }
 
 __global__ __launch_bounds__(kMaskThreads) void valid_mask_kernel(MaskParams p) {
-  __shared__ uint32_t bits[kMaxMaskWords];
+  __shared__ __attribute__((aligned(16))) uint32_t bits[kMaxMaskWords];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int V = p.V, words = p.words;
@@ -79,43 +75,28 @@ __global__ __launch_bounds__(kMaskThreads) void valid_mask_kernel(MaskParams p) 
     mrow = bits;
   }
 
-  // four tokens per group: a group that is all valid is left alone, an all
-  // invalid one is overwritten, a mixed one is blended.  A thread takes
-  // kMaskBatch groups at a time and issues all their loads before the first
-  // store, so their latencies overlap.  The loads are unconditional (a
-  // branch around each would make the compiler wait for each one before
-  // the next): a group that needs no read loads the row's first 16 bytes
-  // instead, which every thread of the row shares in cache.
-  const int n4 = V >> 2;
+  // A wave takes blocks of 256 logits: it reads the block's 8 bitmap words
+  // (two broadcast 16-byte LDS reads), skips the block when all are valid,
+  // and otherwise writes it with four stores of one logit per lane (64
+  // consecutive logits, 256 bytes each) issued for the invalid lanes alone.
+  // Valid logits are neither read nor written: the bytes written are
+  // exactly the -inf entries.
   const float ninf = -INFINITY;
-  for (int g0 = tid; g0 < n4; g0 += kMaskThreads * kMaskBatch) {
-    uint32_t nib[kMaskBatch];
-    float4 v[kMaskBatch];
+  const int lane = tid & 63, hi = lane >> 5, bit = lane & 31;
+  const int n256 = V >> 8;
+  for (int blk = tid >> 6; blk < n256; blk += kMaskThreads / 64) {
+    const uint4 w0 = *reinterpret_cast<const uint4 *>(mrow + blk * 8);
+    const uint4 w1 = *reinterpret_cast<const uint4 *>(mrow + blk * 8 + 4);
+    if ((w0.x & w0.y & w0.z & w0.w & w1.x & w1.y & w1.z & w1.w) == 0xFFFFFFFFu) continue;
+    const uint32_t wd[4] = {hi ? w0.y : w0.x, hi ? w0.w : w0.z, hi ? w1.y : w1.x,
+                            hi ? w1.w : w1.z};
+    float *dst = lg + (int64_t)blk * 256 + lane;
 #pragma unroll
-    for (int u = 0; u < kMaskBatch; ++u) {
-      const int g = g0 + u * kMaskThreads;
-      const int j = g << 2;
-      nib[u] = g < n4 ? (mrow[j >> 5] >> (j & 31)) & 0xFu : 0xFu;
-      const bool mixed = nib[u] != 0xFu && nib[u] != 0u;
-      v[u] = *reinterpret_cast<const float4 *>(lg + (mixed ? j : 0));
-    }
-#pragma unroll
-    for (int u = 0; u < kMaskBatch; ++u) {
-      const int j = (g0 + u * kMaskThreads) << 2;
-      if (nib[u] == 0xFu) continue;
-      float4 w = make_float4(ninf, ninf, ninf, ninf);
-      if (nib[u] != 0u) {
-        w = v[u];
-        if (!(nib[u] & 1u)) w.x = ninf;
-        if (!(nib[u] & 2u)) w.y = ninf;
-        if (!(nib[u] & 4u)) w.z = ninf;
-        if (!(nib[u] & 8u)) w.w = ninf;
-      }
-      __builtin_nontemporal_store(__builtin_bit_cast(f32x4, w), reinterpret_cast<f32x4 *>(lg + j));
-    }
+    for (int q = 0; q < 4; ++q)
+      if (!((wd[q] >> bit) & 1u)) __builtin_nontemporal_store(ninf, dst + 64 * q);
   }
-  for (int j = (n4 << 2) + tid; j < V; j += kMaskThreads)
-    if (!((mrow[j >> 5] >> (j & 31)) & 1u)) lg[j] = ninf;
+  for (int j = (n256 << 8) + tid; j < V; j += kMaskThreads)
+    if (!((mrow[j >> 5] >> (j & 31)) & 1u)) __builtin_nontemporal_store(ninf, lg + j);
 }
 
 __global__ __launch_bounds__(kAdvanceThreads) void trie_advance_kernel(AdvanceParams p) {
