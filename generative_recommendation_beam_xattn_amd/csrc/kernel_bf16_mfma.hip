@@ -133,6 +133,10 @@ __device__ __forceinline__ uint32_t lds_address(const void *p) {
 // preceded by an explicit vmcnt wait and a barrier; the copy counts in vmcnt
 // like any load, in issue order.
 // NT: with the non-temporal hint (data no other workgroup reads soon).
+// An LDS DMA that reads M0 in the instruction right after an M0 write is a
+// hazard on this GPU family (one wait state is required, which the
+// compiler inserts for its own code but cannot see inside asm): each block
+// puts an s_nop between the two.
 template <bool NT = true>
 __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_address(lds_dst));
@@ -141,6 +145,7 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off nt\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
@@ -150,6 +155,7 @@ __device__ __forceinline__ void dma16(const void *src, const void *lds_dst) {
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
@@ -168,6 +174,7 @@ __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, const v
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2 nt\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
@@ -177,6 +184,7 @@ __device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, const v
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
@@ -192,6 +200,7 @@ __device__ __forceinline__ void dma4(const void *src, const void *lds_dst) {
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dword %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
