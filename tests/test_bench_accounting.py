@@ -58,3 +58,43 @@ def test_algorithmic_work_row_by_row(dtype):
         assert work["unique_kv_bytes"] == 2 * kv_rows * w.D * e
         q_bytes = w.R * w.BW * w.Hq * w.D * e
         assert work["bytes"] == work["unique_kv_bytes"] + 2 * q_bytes + work["index_bytes"]
+
+
+def test_stored_traffic_only_for_the_code_it_was_measured_on(tmp_path, monkeypatch):
+    """roofline.traffic comes from profiles/traffic_<workload>.json only while
+    the digest of the device code (HIP sources, headers, build flags) matches
+    the one recorded with the counters."""
+    w = W.custom(name="traffic_probe", seed=0, R=1, L=4, BW=2, steps=[0], Hq=2, Hkv=1, D=64,
+                 dtype="f32")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    path = tmp_path / "profiles" / "traffic_traffic_probe.json"
+    assert bench.stored_traffic(w) is None                  # no record
+    digest = bench.code_digest()                            # of the (empty) tmp tree
+    path.write_text('{"code_sha256_16": "%s", "hbm_bytes_per_launch": 123.0}' % digest)
+    assert bench.stored_traffic(w) == 123.0
+    path.write_text('{"code_sha256_16": "0000000000000000", "hbm_bytes_per_launch": 123.0}')
+    assert bench.stored_traffic(w) is None                  # taken on other code
+
+
+def test_code_digest_covers_sources_headers_and_build_flags(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    src = tmp_path / "generative_recommendation_beam_xattn_amd" / "csrc"
+    src.mkdir(parents=True)
+    (tmp_path / "include").mkdir()
+    files = [src / "api.hip", src / "xattn_internal.h", tmp_path / "include" / "xattn.h",
+             tmp_path / "generative_recommendation_beam_xattn_amd" / "build.py"]
+    for f in files:
+        f.write_text("a")
+    base = bench.code_digest()
+    for f in files:
+        f.write_text("b")
+        assert bench.code_digest() != base, f.name
+        f.write_text("a")
+    assert bench.code_digest() == base
+
+
+def test_data_label_names_each_workload():
+    labels = {bench.data_label(W.make(c, G, R=1)) for c, G in [(2, None), (3, None), (4, None)]}
+    assert len(labels) == 3
+    assert all(lbl.startswith("synthetic") for lbl in labels)
