@@ -557,7 +557,7 @@ def per_beam_leg(m, stream, steps: int) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU; --gpus %d is not supported.  The path shards "
+        print("bench.py: one GPU only; --gpus %d is not supported.  The path shards "
               "by request or KV head with no exchange, so N GPUs would each run this kernel on "
               "their share." % args.gpus, file=sys.stderr)
         sys.exit(2)
