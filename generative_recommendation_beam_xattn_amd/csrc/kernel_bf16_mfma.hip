@@ -45,7 +45,12 @@
 // update.  Deeper chains, resolved into the workspace beforehand, are
 // gathered from global memory by the lanes that hold the row (VALU dot
 // products in fp32).  The debug variant (TAPS) keeps the two stages apart,
-// writes each stage's (m, l, o) and merges them explicitly at the end.
+// writes each stage's (m, l, o) and merges them explicitly at the end.  Its
+// two live states do not fit the registers at D = 128: the compiler spills
+// inside the tile loops, and those scratch accesses count in vmcnt between
+// the tile copies.  So every copy wait in that variant drains vmcnt to 0
+// instead of leaving the newer tiles' copies in flight; the production
+// variant keeps the pipelined counts.
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -1045,25 +1050,25 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
   if (early_walk) {
     if constexpr (kEarlyWalkFits) {
       if (kh == 0)
-        wait_vm_lgkm0<3 * CPW + NKS>();
+        wait_vm_lgkm0<TAPS ? 0 : (3 * CPW + NKS)>();
       else
-        wait_vm_lgkm0<3 * CPW>();
+        wait_vm_lgkm0<TAPS ? 0 : (3 * CPW)>();
     }
     lds_barrier();   // every wave's parent copies have landed
     XATTN_WALK()
     lds_barrier();   // the ancestor slots are visible
     XATTN_ISSUE_BLOCK0()
     // tile 0 and q, older than tiles 1, 2 and block 0
-    wait_vm_lgkm0<2 * CPW + B0PW>();
+    wait_vm_lgkm0<TAPS ? 0 : (2 * CPW + B0PW)>();
     lds_barrier();   // tile 0 and q are visible
   } else {
     // ---- wait for tile 0 (the parent rows and q are older, so they are in
     // too), then the ancestor slots of the block's beams (short chains:
     // walked here, from the parent rows staged in LDS)
     if (n_tiles > 2)
-      wait_vm_lgkm0<2 * CPW>();
+      wait_vm_lgkm0<TAPS ? 0 : (2 * CPW)>();
     else if (n_tiles > 1)
-      wait_vm_lgkm0<CPW>();
+      wait_vm_lgkm0<TAPS ? 0 : CPW>();
     else
       wait_vm_lgkm0<0>();
     if (staged) lds_barrier();   // every wave's parent copies have landed
@@ -1138,11 +1143,11 @@ __global__ __launch_bounds__(RG * KSPLIT * 64) void decode_bf16_kernel(DecodePar
       const bool b0 = t < 2 && lds_tokens;                                            \
       const int units = (cp_prev ? 1 : 0) + (cp_more ? 1 : 0);                        \
       if (b0) {                                                                       \
-        if (units == 0) wait_vm_lgkm0<B0PW>();                                        \
-        else wait_vm_lgkm0<B0PW + CPW>();                                             \
+        if (units == 0) wait_vm_lgkm0<TAPS ? 0 : B0PW>();                             \
+        else wait_vm_lgkm0<TAPS ? 0 : (B0PW + CPW)>();                                \
       } else {                                                                        \
         if (units == 0) wait_vm_lgkm0<0>();                                           \
-        else wait_vm_lgkm0<CPW>();                                                    \
+        else wait_vm_lgkm0<TAPS ? 0 : CPW>();                                         \
       }                                                                               \
     }                                                                                 \
     lds_barrier();                                                                    \
@@ -1552,7 +1557,7 @@ void decode_bf16_paired_kernel(DecodeParams p) {
   // ---- the parent rows and q are in (older than the speculative tiles);
   // walk the ancestor chains of the block's beams, take q into registers
   if (speculate)
-    wait_vm_lgkm0<2 * CPW>();
+    wait_vm_lgkm0<TAPS ? 0 : (2 * CPW)>();
   else
     wait_vm_lgkm0<0>();
   lds_barrier();   // every wave's parent and q copies have landed
@@ -1611,9 +1616,9 @@ void decode_bf16_paired_kernel(DecodeParams p) {
 
   // ---- tile 0 is in once all but the copies younger than it are
   if (n_tiles > 2)
-    wait_vm_lgkm0<2 * CPW>();
+    wait_vm_lgkm0<TAPS ? 0 : (2 * CPW)>();
   else if (n_tiles > 1)
-    wait_vm_lgkm0<CPW>();
+    wait_vm_lgkm0<TAPS ? 0 : CPW>();
   else
     wait_vm_lgkm0<0>();
   lds_barrier();   // tile 0 is visible
@@ -1638,7 +1643,7 @@ void decode_bf16_paired_kernel(DecodeParams p) {
     /* tile t + 1 is in once all but the copy younger than it (tile t + 2, */         \
     /* copied at step t - 1 or, for t = 0, in the prologue) are */                   \
     if (t + 2 < n_tiles)                                                              \
-      wait_vm_lgkm0<CPW>();                                                           \
+      wait_vm_lgkm0<TAPS ? 0 : CPW>();                                                \
     else                                                                              \
       wait_vm_lgkm0<0>();                                                             \
     lds_barrier();                                                                    \
