@@ -13,7 +13,11 @@
 // chunk of all BW rows -- and stages it whole in LDS before writing any of
 // it: all reads precede all writes, behind a barrier, and no other
 // workgroup touches those bytes.  Splitting the slice by K/V and columns
-// spreads a level's few slices over many workgroups.  Rows whose parent is
+// spreads a level's few slices over many workgroups.  A chunk is a whole
+// 128-byte cache line of each row where the stage allows it: with narrower
+// chunks two workgroups write the two halves of one line, and a partial
+// line costs the memory side a merge with the line's old contents (1.3-1.4x
+// the time of whole lines at 256 and 512 beams).  Rows whose parent is
 // themselves are not rewritten, and a slice whose parents are all the
 // identity is not written at all (its rows are read with the parents, in
 // the same round trip).
@@ -25,8 +29,13 @@ namespace xattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStageBytes = 32 * 1024;
-static_assert(kStageBytes <= kThreads * 8 * 16, "8 units per thread cover the stage");
+// Largest stage (BW rows of one column chunk), and the widest chunk.  The
+// stage is sized per launch, not to this bound: a workgroup holds only what
+// it moves, so more workgroups fit a compute unit's LDS and more rows are in
+// flight at once.  Chunks wider than a cache line measured no faster.
+constexpr int kStageBytes = 64 * 1024;
+constexpr int kChunkMaxBytes = 128;
+static_assert(kStageBytes <= kThreads * 16 * 16, "16 units per thread cover the stage");
 static_assert(kMaxReorderBeams <= kThreads * 8, "8 parent slots per thread cover the beams");
 
 // UPT: 16-byte units of the stage per thread, PPT: parent slots per thread
@@ -34,9 +43,11 @@ static_assert(kMaxReorderBeams <= kThreads * 8, "8 parent slots per thread cover
 // issues all of its loads before it waits and none of them is redundant.
 template <int UPT, int PPT>
 __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytes];
+  // dynamic LDS: the stage (BW rows x chunk_bytes), then BW parent slots
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ int moved;
-  extern __shared__ int32_t par[];   // BW parent slots (dynamic)
+  uint8_t *stage = smem;
+  int32_t *par = reinterpret_cast<int32_t *>(smem + (int64_t)p.BW * p.chunk_bytes);
 
   const int tid = threadIdx.x;
   const int n_cc = (int)(p.row_bytes / p.chunk_bytes);   // column chunks per row
@@ -117,40 +128,42 @@ hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, L
       (int64_t)p.BW * p.chunk_bytes > kStageBytes || p.chunk_bytes % 16 != 0 ||
       p.row_bytes % p.chunk_bytes != 0)
     return hipErrorInvalidConfiguration;
-  auto pow2_cover = [](int64_t n) {   // smallest of 1, 2, 4, 8 with 256 * it >= n
+  auto pow2_cover = [](int64_t n) {   // smallest of 1, 2, 4, 8, 16 with 256 * it >= n
     int x = 1;
-    while (x < 8 && (int64_t)x * kThreads < n) x *= 2;
+    while (x < 16 && (int64_t)x * kThreads < n) x *= 2;
     return x;
   };
   const int upt = pow2_cover((int64_t)p.BW * (p.chunk_bytes / 16));
-  const int ppt = pow2_cover(p.BW) == 1 ? 1 : 8;
+  const int ppt = p.BW <= kThreads ? 1 : 8;
+  const size_t lds = (size_t)p.BW * (p.chunk_bytes + sizeof(int32_t));
   auto go = [&](auto kernel) {
     if (ev.start || ev.stop)
-      hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads),
-                            (size_t)p.BW * sizeof(int32_t), stream, ev.start, ev.stop, 0u, p);
+      hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, stream, ev.start,
+                            ev.stop, 0u, p);
     else
-      hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads),
-                         (size_t)p.BW * sizeof(int32_t), stream, p);
+      hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
   };
   if (ppt == 1) {
     if (upt == 1) go(reorder_unshared_kernel<1, 1>);
     else if (upt == 2) go(reorder_unshared_kernel<2, 1>);
     else if (upt == 4) go(reorder_unshared_kernel<4, 1>);
-    else go(reorder_unshared_kernel<8, 1>);
+    else if (upt == 8) go(reorder_unshared_kernel<8, 1>);
+    else go(reorder_unshared_kernel<16, 1>);
   } else {
     if (upt == 1) go(reorder_unshared_kernel<1, 8>);
     else if (upt == 2) go(reorder_unshared_kernel<2, 8>);
     else if (upt == 4) go(reorder_unshared_kernel<4, 8>);
-    else go(reorder_unshared_kernel<8, 8>);
+    else if (upt == 8) go(reorder_unshared_kernel<8, 8>);
+    else go(reorder_unshared_kernel<16, 8>);
   }
   return hipGetLastError();
 }
 
 int64_t reorder_chunk_bytes(int64_t row_bytes, int32_t BW) {
-  // the largest power-of-two divisor of the row that lets BW rows fit LDS,
-  // and at most 64 bytes: more, smaller workgroups per slice
+  // the largest power-of-two divisor of the row that lets BW rows fit the
+  // stage, and at most one cache line: more, smaller workgroups per slice
   int64_t c = row_bytes;
-  while (c > 16 && ((int64_t)BW * c > kStageBytes || c > 64)) c /= 2;
+  while (c > 16 && ((int64_t)BW * c > kStageBytes || c > kChunkMaxBytes)) c /= 2;
   return c;
 }
 
