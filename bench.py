@@ -214,19 +214,39 @@ def cpu_baseline(w, target_s: float) -> dict:
 
 # ------------------------------------------------------- Unshared-cache reorder
 
+def reorder_bytes(parent: np.ndarray, Hkv: int, row_bytes: int, levels: int) -> int:
+    """Compulsory bytes of one in-place reorder of `levels` levels with
+    parents `parent` [R][BW]: per request, every row whose parent is another
+    slot is written, and every distinct slot such a row takes its history
+    from is read, at each level, K and V, for every KV head."""
+    par = np.asarray(parent)
+    mv = par != np.arange(par.shape[1])[None, :]
+    moved = int(mv.sum())
+    sources = sum(int(np.unique(par[r][mv[r]]).size) for r in range(par.shape[0]))
+    return 2 * Hkv * levels * row_bytes * (sources + moved)
+
+
 def reorder_leg(w, copies, steps: int, stream) -> dict | None:
     """xattn_reorder_unshared as a caller would run it after each selection:
     at every decode level s >= 1 of the workload, levels 0..s-1 take the
     rows of parent_idx[:, s, :].  Timed per launch with events bound to the
-    dispatch, on the rotation copies (so rows come from HBM).  Algorithmic
-    bytes: every row of a slice read once and every moved row written once,
-    K and V; a slice with identity parents moves nothing."""
+    dispatch.  Each launch works on the next of a rotation of Unshared
+    caches holding >= 1 GiB together (the decode run's copies, plus clones
+    where those hold less), so that no launch finds its rows in the 256 MB
+    last-level cache.  Algorithmic bytes, K and V: every row that moves
+    written once, and every distinct row it takes its history from read once
+    (rows that keep their place are neither read nor written)."""
     import torch
     from generative_recommendation_beam_xattn_amd import binding as B
     levels = [s for s in w.steps if s >= 1]
     if not levels or w.BW > 2048:
         return None
-    n_rot = len(copies)
+    per_set = 2 * copies[0]["uk"].numel() * copies[0]["uk"].element_size()
+    n_sets = max(len(copies), math.ceil((1 << 30) / per_set))
+    sets = [(c["uk"], c["uv"]) for c in copies]
+    sets += [(copies[0]["uk"].clone(), copies[0]["uv"].clone())
+             for _ in range(n_sets - len(copies))]
+    par = copies[0]["par"]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in levels] for _ in range(steps + 1)]
     for row in ev:
@@ -234,23 +254,23 @@ def reorder_leg(w, copies, steps: int, stream) -> dict | None:
             a.record(stream)
             b.record(stream)
     torch.cuda.synchronize()
+    n = 0
     for k in range(steps + 1):      # round 0 is a warmup
-        c = copies[k % n_rot]
         for i, s in enumerate(levels):
-            B.reorder_unshared(c["uk"], c["uv"], c["par"][:, s, :], s, stream=stream,
-                               events=ev[k][i])
+            uk, uv = sets[n % n_sets]
+            n += 1
+            B.reorder_unshared(uk, uv, par[:, s, :], s, stream=stream, events=ev[k][i])
     torch.cuda.synchronize()
+    del sets
     us = np.array([[a.elapsed_time(b) * 1e3 for a, b in ev[k]] for k in range(1, steps + 1)])
     row = w.D * w.elem_bytes
     by_level = []
     for i, s in enumerate(levels):
-        moved = int(np.sum(w.parent_idx[:, s, :] != np.arange(w.BW)[None, :]))
-        moving_req = int(np.sum(np.any(w.parent_idx[:, s, :] != np.arange(w.BW)[None, :], axis=1)))
-        byts = 2 * w.Hkv * s * row * (moving_req * w.BW + moved)
+        byts = reorder_bytes(w.parent_idx[:, s, :], w.Hkv, row, s)
         t = float(us[:, i].mean())
         by_level.append({"level": s, "levels_moved": s, "kernel_us": t, "bytes": byts,
                          "GBps": byts / t / 1e3, "frac_of_hbm_peak": byts / t / 1e3 / HBM_PEAK_GBS})
-    return {"by_level": by_level, "bound": "hbm", "steps": steps}
+    return {"by_level": by_level, "bound": "hbm", "steps": steps, "cache_sets": n_sets}
 
 
 # ------------------------------------------------------------ valid-path masks

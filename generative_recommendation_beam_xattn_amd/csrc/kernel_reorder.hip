@@ -10,17 +10,19 @@
 // Hazards.  A row may be the source of several beams and the destination of
 // another, so rows cannot be moved one by one.  One workgroup owns one
 // column chunk of K or of V of one (request, KV head, level) slice -- that
-// chunk of all BW rows -- and stages it whole in LDS before writing any of
-// it: all reads precede all writes, behind a barrier, and no other
-// workgroup touches those bytes.  Splitting the slice by K/V and columns
-// spreads a level's few slices over many workgroups.  A chunk is a whole
-// 128-byte cache line of each row where the stage allows it: with narrower
-// chunks two workgroups write the two halves of one line, and a partial
-// line costs the memory side a merge with the line's old contents (1.3-1.4x
-// the time of whole lines at 256 and 512 beams).  Rows whose parent is
-// themselves are not rewritten, and a slice whose parents are all the
-// identity is not written at all (its rows are read with the parents, in
-// the same round trip).
+// chunk of all BW rows -- and gathers, for every row that moves, its
+// parent's chunk into registers; every wave waits for all of its loads and
+// the workgroup synchronises before any thread writes.  All reads of the
+// chunk thus precede all writes, and no other workgroup touches those
+// bytes.  Rows whose parent is themselves are not written; a row is read
+// once per beam it is the parent of, the repeats from the caches.
+// Splitting the slice by K/V and columns spreads a level's few slices over
+// many workgroups.  A chunk is a whole 128-byte cache line of each row where
+// the registers allow it: with narrower chunks two workgroups write the two
+// halves of one line, and a partial line costs the memory side a merge with
+// the line's old contents (1.3-1.4x the time of whole lines at 256 and 512
+// beams).  Keeping the chunk in registers rather than staging it in LDS
+// leaves a compute unit's workgroup count to its waves, not to its LDS.
 #include <hip/hip_ext.h>
 
 #include "xattn_internal.h"
@@ -28,26 +30,24 @@
 namespace xattn {
 namespace {
 
+// (a native vector type: the HIP uint4 struct kept across the barrier is
+// not split into registers and goes to scratch)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
-// Largest stage (BW rows of one column chunk), and the widest chunk.  The
-// stage is sized per launch, not to this bound: a workgroup holds only what
-// it moves, so more workgroups fit a compute unit's LDS and more rows are in
-// flight at once.  Chunks wider than a cache line measured no faster.
+// Largest column chunk of a slice a workgroup holds in registers (BW rows x
+// chunk bytes, at most 16 units of 16 bytes per thread), and the widest
+// chunk: a cache line (wider chunks measured no faster).
 constexpr int kStageBytes = 64 * 1024;
 constexpr int kChunkMaxBytes = 128;
-static_assert(kStageBytes <= kThreads * 16 * 16, "16 units per thread cover the stage");
+static_assert(kStageBytes <= kThreads * 16 * 16, "16 units per thread cover the chunk");
 static_assert(kMaxReorderBeams <= kThreads * 8, "8 parent slots per thread cover the beams");
 
-// UPT: 16-byte units of the stage per thread, PPT: parent slots per thread
-// (each the smallest power of two that covers the launch), so every thread
-// issues all of its loads before it waits and none of them is redundant.
-template <int UPT, int PPT>
+// UPT: 16-byte units of the chunk per thread, the smallest power of two that
+// covers the launch.
+template <int UPT>
 __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParams p) {
-  // dynamic LDS: the stage (BW rows x chunk_bytes), then BW parent slots
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int moved;
-  uint8_t *stage = smem;
-  int32_t *par = reinterpret_cast<int32_t *>(smem + (int64_t)p.BW * p.chunk_bytes);
+  extern __shared__ int32_t par[];   // BW parent slots (dynamic)
 
   const int tid = threadIdx.x;
   const int n_cc = (int)(p.row_bytes / p.chunk_bytes);   // column chunks per row
@@ -66,54 +66,47 @@ __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParam
   uint8_t *base = static_cast<uint8_t *>(part < n_cc ? p.unshared_k : p.unshared_v) + slice;
   const int64_t c0 = (int64_t)(part % n_cc) * p.chunk_bytes;
 
-  // The parent slots and columns [c0, c0 + chunk) of every row of the slice
-  // are loaded together (one memory round trip, not one for the parents and
-  // then one for the rows).
-  if (tid == 0) moved = 0;
-  // this thread's parent slots, loaded into registers first and stored to
-  // LDS only after the row loads are issued (indices past BW repeat the
-  // last slot and are not stored)
-  int32_t pr[PPT];
-#pragma unroll
-  for (int i = 0; i < PPT; ++i)
-    pr[i] = p.parent[(int64_t)r * p.parent_stride + min(tid + i * kThreads, BW - 1)];
   {
-    uint4 v[UPT];
+    // the parent slots, all of the thread's loads in flight together
+    int32_t pv[kMaxReorderBeams / kThreads];
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = min(tid + i * kThreads, n_units - 1);
-      const int b = u / units_per_row, c = u - b * units_per_row;
-      v[i] = *reinterpret_cast<const uint4 *>(base + (int64_t)b * RB + c0 + c * 16);
+    for (int j = 0; j < kMaxReorderBeams / kThreads; ++j) {
+      const int b = tid + j * kThreads;
+      if (b < BW) pv[j] = p.parent[(int64_t)r * p.parent_stride + b];
     }
-    // (units past the end, in the last round only, repeat the last one: the
-    // same bytes to the same place, with no branch to hold the loads apart)
 #pragma unroll
-    for (int i = 0; i < UPT; ++i) {
-      const int u = min(tid + i * kThreads, n_units - 1);
-      *reinterpret_cast<uint4 *>(stage + (int64_t)u * 16) = v[i];
+    for (int j = 0; j < kMaxReorderBeams / kThreads; ++j) {
+      const int b = tid + j * kThreads;
+      if (b < BW) par[b] = min(max(pv[j], 0), BW - 1);
     }
   }
-  int mine = 0;
-#pragma unroll
-  for (int i = 0; i < PPT; ++i) {
-    const int b = tid + i * kThreads;
-    if (b < BW) {
-      const int a = min(max(pr[i], 0), BW - 1);
-      par[b] = a;
-      mine |= a != b;
-    }
-  }
-  __syncthreads();   // moved = 0 is visible before any thread sets it
-  if (mine) moved = 1;   // benign race: every writer stores 1
   __syncthreads();
-  if (!moved) return;
-  // every read of this chunk is done (the barriers above): write the moved rows
-  for (int u = tid; u < n_units; u += kThreads) {
+  // each unit of a moved row takes the same unit of its parent's row,
+  // gathered into registers (every unit loads, with no branch to hold the
+  // loads apart; units past the end repeat the last one); only moved rows
+  // are written
+  u32x4 v[UPT];
+  uint32_t mv = 0;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int u = min(tid + i * kThreads, n_units - 1);
     const int b = u / units_per_row, c = u - b * units_per_row;
     const int a = par[b];
-    if (a != b)
-      *reinterpret_cast<uint4 *>(base + (int64_t)b * RB + c0 + c * 16) =
-          *reinterpret_cast<const uint4 *>(stage + ((int64_t)a * units_per_row + c) * 16);
+    v[i] = *reinterpret_cast<const u32x4 *>(base + (int64_t)a * RB + c0 + c * 16);
+    mv |= (uint32_t)(a != b && tid + i * kThreads < n_units) << i;
+  }
+  // A row may be one beam's source and another's destination: every load of
+  // the workgroup has returned (vmcnt 0 in each wave, then the barrier)
+  // before any thread writes.
+  __builtin_amdgcn_s_waitcnt(0x70);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    if ((mv >> i) & 1u) {
+      const int u = tid + i * kThreads;
+      const int b = u / units_per_row, c = u - b * units_per_row;
+      *reinterpret_cast<u32x4 *>(base + (int64_t)b * RB + c0 + c * 16) = v[i];
+    }
   }
 }
 
@@ -134,8 +127,7 @@ hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, L
     return x;
   };
   const int upt = pow2_cover((int64_t)p.BW * (p.chunk_bytes / 16));
-  const int ppt = p.BW <= kThreads ? 1 : 8;
-  const size_t lds = (size_t)p.BW * (p.chunk_bytes + sizeof(int32_t));
+  const size_t lds = (size_t)p.BW * sizeof(int32_t);
   auto go = [&](auto kernel) {
     if (ev.start || ev.stop)
       hipExtLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, stream, ev.start,
@@ -143,25 +135,18 @@ hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, L
     else
       hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kThreads), lds, stream, p);
   };
-  if (ppt == 1) {
-    if (upt == 1) go(reorder_unshared_kernel<1, 1>);
-    else if (upt == 2) go(reorder_unshared_kernel<2, 1>);
-    else if (upt == 4) go(reorder_unshared_kernel<4, 1>);
-    else if (upt == 8) go(reorder_unshared_kernel<8, 1>);
-    else go(reorder_unshared_kernel<16, 1>);
-  } else {
-    if (upt == 1) go(reorder_unshared_kernel<1, 8>);
-    else if (upt == 2) go(reorder_unshared_kernel<2, 8>);
-    else if (upt == 4) go(reorder_unshared_kernel<4, 8>);
-    else if (upt == 8) go(reorder_unshared_kernel<8, 8>);
-    else go(reorder_unshared_kernel<16, 8>);
-  }
+  if (upt == 1) go(reorder_unshared_kernel<1>);
+  else if (upt == 2) go(reorder_unshared_kernel<2>);
+  else if (upt == 4) go(reorder_unshared_kernel<4>);
+  else if (upt == 8) go(reorder_unshared_kernel<8>);
+  else go(reorder_unshared_kernel<16>);
   return hipGetLastError();
 }
 
 int64_t reorder_chunk_bytes(int64_t row_bytes, int32_t BW) {
-  // the largest power-of-two divisor of the row that lets BW rows fit the
-  // stage, and at most one cache line: more, smaller workgroups per slice
+  // the largest power-of-two divisor of the row that lets BW rows fit a
+  // workgroup's registers, and at most one cache line: more, smaller
+  // workgroups per slice
   int64_t c = row_bytes;
   while (c > 16 && ((int64_t)BW * c > kStageBytes || c > kChunkMaxBytes)) c /= 2;
   return c;

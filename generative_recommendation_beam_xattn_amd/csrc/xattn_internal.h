@@ -119,7 +119,7 @@ struct ReorderParams {
   const int32_t *parent;   // [R] rows of BW, stride parent_stride
   int64_t parent_stride;
   int64_t row_bytes;       // D * element size
-  int64_t chunk_bytes;     // columns staged per pass (divides row_bytes)
+  int64_t chunk_bytes;     // columns per workgroup (divides row_bytes)
   int32_t R, Hkv, S, BW, n_levels;
 };
 hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream,

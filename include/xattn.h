@@ -268,10 +268,10 @@ xattn_status xattn_decode_per_beam_timed(const xattn_shape *shape, const void *q
  *   n_levels     0 <= n_levels <= S; levels >= n_levels are not touched
  *
  * Typical use after the selection that yields the parents of level s+1:
- * reorder levels 0..s with them, then write level s+1 of every slot.  Every
- * slice (request, KV head, level) is staged whole before any of its rows is
- * written, so the result is as if all rows were read before any was
- * written.  shape supplies R, BW, Hkv, D, S and dtype (head counts and
+ * reorder levels 0..s with them, then write level s+1 of every slot.  Within
+ * every slice (request, KV head, level), all reads of a column range finish
+ * before any of its rows is written, so the result is as if all rows were
+ * read before any was written.  shape supplies R, BW, Hkv, D, S and dtype (head counts and
  * max_prompt_len must be valid but are otherwise unused); beam_width up to
  * 2048 (XATTN_EUNSUPPORTED above).  Calls on one cache must not overlap
  * each other or an attention call reading it.  The _timed form binds two

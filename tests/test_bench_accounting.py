@@ -98,3 +98,27 @@ def test_data_label_names_each_workload():
     labels = {bench.data_label(W.make(c, G, R=1)) for c, G in [(2, None), (3, None), (4, None)]}
     assert len(labels) == 3
     assert all(lbl.startswith("synthetic") for lbl in labels)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_reorder_bytes_count_moved_rows_and_distinct_sources(seed):
+    # brute force: walk every slot, collect the rows written and the rows read
+    rng = np.random.default_rng(seed)
+    R, BW, Hkv, row, levels = 3, 9, 2, 256, 2
+    par = rng.integers(0, BW, size=(R, BW)).astype(np.int32)
+    par[0] = np.arange(BW)                     # a request whose beams all stay
+    par[1, :4] = np.arange(4)                  # some stay, the rest move
+    written = read = 0
+    for r in range(R):
+        srcs = set()
+        for b in range(BW):
+            if par[r, b] != b:
+                written += 1
+                srcs.add(int(par[r, b]))
+        read += len(srcs)
+    want = 2 * Hkv * levels * row * (written + read)
+    assert bench.reorder_bytes(par, Hkv, row, levels) == want
+    assert bench.reorder_bytes(np.tile(np.arange(BW), (R, 1)), Hkv, row, levels) == 0
+    # every beam from one parent: BW - 1 rows written, one row read
+    one = np.zeros((1, BW), np.int32)
+    assert bench.reorder_bytes(one, 1, row, 1) == 2 * row * (BW - 1 + 1)
