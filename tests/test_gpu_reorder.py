@@ -51,6 +51,31 @@ def test_reorder_matches_oracle(R, Hkv, S, BW, D, dtype, n_levels):
     assert same_bits(dv, oracle.reorder_unshared(uv, parent, n_levels))
 
 
+@pytest.mark.parametrize("BW,D,dtype", [(37, 64, "f32"), (256, 128, "bf16"), (512, 128, "bf16"),
+                                         (2048, 128, "bf16")])
+def test_reorder_structured_parents(BW, D, dtype):
+    # per request: every beam stays (nothing is read or written); every beam
+    # descends from one slot (one source, BW - 1 destinations); half stay and
+    # the other half reverse their order (each moved row is both a source
+    # and a destination)
+    say("[reorder structured] BW=%d D=%d %s" % (BW, D, dtype))
+    R, Hkv, S, n_levels = 3, 2, 3, 2
+    rng = np.random.default_rng(BW + D)
+    uk = W.normal(rng, (R, Hkv, S, BW, D), dtype)
+    uv = W.normal(rng, (R, Hkv, S, BW, D), dtype)
+    par = np.empty((R, BW), np.int32)
+    par[0] = np.arange(BW)
+    par[1] = BW // 3
+    half = BW // 2
+    par[2, :half] = np.arange(half)
+    par[2, half:] = np.arange(BW - 1, half - 1, -1)
+    dk, dv = to_dev(uk), to_dev(uv)
+    X.reorder_unshared(dk, dv, to_dev(par), n_levels)
+    torch.cuda.synchronize()
+    assert same_bits(dk, oracle.reorder_unshared(uk, par, n_levels))
+    assert same_bits(dv, oracle.reorder_unshared(uv, par, n_levels))
+
+
 def test_identity_parents_leave_the_cache_alone():
     rng = np.random.default_rng(5)
     uk = W.normal(rng, (2, 2, 3, 64, 128), "bf16")
