@@ -100,12 +100,14 @@ __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParam
   // before any thread writes.
   __builtin_amdgcn_s_waitcnt(0x70);
   __syncthreads();
+  // (written once: past the caches)
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     if ((mv >> i) & 1u) {
       const int u = tid + i * kThreads;
       const int b = u / units_per_row, c = u - b * units_per_row;
-      *reinterpret_cast<u32x4 *>(base + (int64_t)b * RB + c0 + c * 16) = v[i];
+      __builtin_nontemporal_store(v[i],
+                                  reinterpret_cast<u32x4 *>(base + (int64_t)b * RB + c0 + c * 16));
     }
   }
 }
