@@ -38,9 +38,9 @@ constexpr int kThreads = 256;
 // Largest column chunk of a slice a workgroup holds in registers (BW rows x
 // chunk bytes, at most 16 units of 16 bytes per thread), and the widest
 // chunk: a cache line (wider chunks measured no faster).
-constexpr int kStageBytes = 64 * 1024;
+constexpr int kChunkLimitBytes = 64 * 1024;
 constexpr int kChunkMaxBytes = 128;
-static_assert(kStageBytes <= kThreads * 16 * 16, "16 units per thread cover the chunk");
+static_assert(kChunkLimitBytes <= kThreads * 16 * 16, "16 units per thread cover the chunk");
 static_assert(kMaxReorderBeams <= kThreads * 8, "8 parent slots per thread cover the beams");
 
 // UPT: 16-byte units of the chunk per thread, the smallest power of two that
@@ -97,7 +97,8 @@ __global__ __launch_bounds__(kThreads) void reorder_unshared_kernel(ReorderParam
   }
   // A row may be one beam's source and another's destination: every load of
   // the workgroup has returned (vmcnt 0 in each wave, then the barrier)
-  // before any thread writes.
+  // before any thread writes.  s_waitcnt immediate (gfx9 encoding): vmcnt 0
+  // in bits 3:0 and 15:14, expcnt left at 7 in bits 6:4, lgkmcnt 0 in 11:8.
   __builtin_amdgcn_s_waitcnt(0x70);
   __syncthreads();
   // (written once: past the caches)
@@ -120,7 +121,7 @@ hipError_t launch_reorder_unshared(const ReorderParams &p, hipStream_t stream, L
   const int64_t grid = (int64_t)p.R * p.Hkv * p.n_levels * 2 * (p.row_bytes / p.chunk_bytes);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff || p.BW > kMaxReorderBeams || p.chunk_bytes <= 0 ||
-      (int64_t)p.BW * p.chunk_bytes > kStageBytes || p.chunk_bytes % 16 != 0 ||
+      (int64_t)p.BW * p.chunk_bytes > kChunkLimitBytes || p.chunk_bytes % 16 != 0 ||
       p.row_bytes % p.chunk_bytes != 0)
     return hipErrorInvalidConfiguration;
   auto pow2_cover = [](int64_t n) {   // smallest of 1, 2, 4, 8, 16 with 256 * it >= n
@@ -150,7 +151,7 @@ int64_t reorder_chunk_bytes(int64_t row_bytes, int32_t BW) {
   // workgroup's registers, and at most one cache line: more, smaller
   // workgroups per slice
   int64_t c = row_bytes;
-  while (c > 16 && ((int64_t)BW * c > kStageBytes || c > kChunkMaxBytes)) c /= 2;
+  while (c > 16 && ((int64_t)BW * c > kChunkLimitBytes || c > kChunkMaxBytes)) c /= 2;
   return c;
 }
 
