@@ -55,11 +55,18 @@ __global__ __launch_bounds__(kMaskThreads) void valid_mask_kernel(MaskParams p) 
     mrow = bits;
   } else if (p.dense) {
     // the node's dense row into LDS with one coalesced load per thread, so
-    // the groups below test bits without a global round trip each
+    // the groups below test bits without a global round trip each; a row
+    // with every bit set (every next token valid, as at a root whose
+    // children cover the vocabulary) has nothing to write
     const uint32_t *src = reinterpret_cast<const uint32_t *>(p.table + p.mask_off) +
                           (int64_t)n * words;
-    for (int w = tid; w < words; w += kMaskThreads) bits[w] = src[w];
-    __syncthreads();
+    uint32_t all = 0xFFFFFFFFu;
+    for (int w = tid; w < words; w += kMaskThreads) {
+      const uint32_t x = src[w];
+      bits[w] = x;
+      all &= x;
+    }
+    if (__syncthreads_and(all == 0xFFFFFFFFu)) return;
     mrow = bits;
   } else {
     for (int w = tid; w < words; w += kMaskThreads) bits[w] = 0u;
